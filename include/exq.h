@@ -1,0 +1,148 @@
+/*
+ * exq -- mixed-bitrate quantized linear layers on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is a linear layer y = x * W^T whose weight W ([N][K], N
+ * outputs, K inputs) is stored EXL2-style: every group of 128 consecutive
+ * input channels has its own bit width from {2,3,4,5,6,8}, the widths of one
+ * layer are mixed toward a target average bits-per-weight, and the groups
+ * judged important are kept at higher width.  Sources: the exllamav2
+ * repository report (nightvoyager.top), sections "innovations" and "key
+ * design decisions" (arbitrary average bitrate, several bitrates spliced
+ * inside one layer, important columns at higher bits); the promptquorum.com
+ * "ExLlamaV2 explained" page, section "what is EXL2 quantization" (2/3/4/5/6/8
+ * bit mixed to an average such as 2.55 bits per weight).  The weights are
+ * dequantized on the fly inside the matmul kernels (the Q-GEMM of the
+ * exllamav2 report's "solution philosophy"), never materialized.
+ *
+ * Readings fixed here because the pages give none:
+ *   - one fp16 scale per (group, output column), symmetric round-to-nearest:
+ *     s = fp16(max|w| / (2^(b-1) - 1)), code c = clamp(rint(w / s)) + 2^(b-1);
+ *   - dequantized weight w_hat = fp16_RNE((c - 2^(b-1)) * s);
+ *   - the EXQ1 bit layout below.
+ *
+ * EXQ1 layout (group size 128, G = K/128, widths b_g, P_g = sum_{h<g} b_h):
+ *   qweight: one byte buffer of sum_g 16*N*b_g bytes, no padding.  Group g of
+ *   column n owns b_g 16-byte words; word j is at byte 16*(N*P_g + j*N + n),
+ *   so 64 consecutive columns read one contiguous kilobyte.  A column's
+ *   dwords are numbered m = 4*j + r (r = dword in the word, little endian).
+ *   Widths split into planes, low bits first: 2:[2] 3:[2,1] 4:[4] 5:[4,1]
+ *   6:[4,2] 8:[8].  For code k in [0,128): u = k/4, e = k%4, e1 = e%2,
+ *   e2 = e/2.  Plane 0 (width p0, dwords [0, 4*p0)): per = 8/p0; dword u/per,
+ *   bit p0*(u%per) + 8*e2 + 16*e1.  Plane 1 (width p1, dwords
+ *   [4*p0, 4*p0+4*p1)): with d = u/per and R = p0/p1, dword 4*p0 + d/R, bit
+ *   p0*(u%per) + 16*e1 + p1*(d%R) + 8*e2.  Every field lies inside one dword.
+ *   scales: fp16 [G][N] row-major, s(g, n) at g*N + n.
+ *
+ * Conventions for every entry point:
+ *   - "device" pointers are HIP device memory on the current device; "host"
+ *     pointers are ordinary host memory.  fp16 values are IEEE binary16 bit
+ *     patterns (uint16_t).
+ *   - streams are hipStream_t values passed as void* (NULL = null stream).
+ *     Launching calls are asynchronous and never synchronize; faults inside a
+ *     kernel surface at the caller's next synchronization.
+ *   - arguments are validated before anything is launched; a failed call
+ *     launches nothing and leaves outputs untouched.
+ *   - results are deterministic: the same inputs give the same bits.
+ */
+#ifndef EXQ_H
+#define EXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EXQ_OK = 0,
+    EXQ_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad width, non-finite input */
+    EXQ_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (e.g. group size != 128) */
+    EXQ_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+    EXQ_ERR_OOM = 4          /* device or host allocation failed */
+} exq_status;
+
+typedef struct exq_layer* exq_layer_t;
+typedef struct exq_plan* exq_plan_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* exq_status_string(exq_status s);
+
+/* Text of the last error detected on the calling thread (static per-thread
+ * buffer, "" if none). */
+const char* exq_last_error(void);
+
+/* ----------------------------------------------------------- host packer */
+
+/* Bytes of EXQ1 qweight storage for a layer: sum_g b_g * group_size * N / 8.
+ * widths: host, K/group_size entries.  Returns 0 if any argument is invalid
+ * (K or N <= 0, group_size != 128, K % 128 != 0, width not in {2,3,4,5,6,8}). */
+size_t exq_packed_bytes(int K, int N, int group_size, const uint8_t* widths);
+
+/* Quantize and pack a layer on the host (offline step, multi-threaded).
+ *   W           host, fp32 [N][K] row-major (nn.Linear weight layout)
+ *   widths      host, uint8 [K/group_size], each in {2,3,4,5,6,8}
+ *   qweight_out host, exq_packed_bytes() bytes, written completely
+ *   scales_out  host, fp16 [K/group_size][N]
+ * Quantizer: per (group g, column n), s = fp16_RNE(fp32(max|w|) / fp32(2^(b-1)-1))
+ * with an fp32 division; code c = clamp(rint_even(fp32(w)/fp32(s)),
+ * -(2^(b-1)-1), 2^(b-1)-1) + 2^(b-1); if s == 0 all codes are 2^(b-1).
+ * Errors: EXQ_ERR_INVALID_ARG for bad sizes/pointers/widths, non-finite W,
+ * or a scale that overflows fp16; EXQ_ERR_UNSUPPORTED for group_size != 128. */
+exq_status exq_pack(const float* W, int K, int N, int group_size, const uint8_t* widths,
+                    void* qweight_out, uint16_t* scales_out);
+
+/* --------------------------------------------------------- device layers */
+
+/* Describe a packed layer already resident in device memory.
+ *   K, N        in/out features; K % 128 == 0, N % 64 == 0, both > 0
+ *   widths_host host, uint8 [K/128]; copied, the caller may free it
+ *   d_qweight   device, 16-byte aligned EXQ1 words (borrowed: must outlive the handle)
+ *   d_scales    device, 16-byte aligned fp16 [G][N] (borrowed)
+ * The handle owns small device metadata and a split-K workspace; it may be
+ * used by one stream at a time.  Errors: INVALID_ARG, UNSUPPORTED
+ * (group_size != 128), OOM, HIP. */
+exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_host,
+                            const void* d_qweight, const void* d_scales, exq_layer_t* out);
+
+/* Release a handle and what it owns (not the borrowed buffers).  NULL is a no-op.
+ * The caller must make sure no launched work still uses the handle. */
+void exq_layer_destroy(exq_layer_t layer);
+
+/* y = x * W_hat^T on `stream`.
+ *   x  device, fp16 [M][K] row-major, 16-byte aligned
+ *   y  device, fp16 [M][N] row-major, 16-byte aligned, must not overlap x
+ *   M >= 1.  M <= 16 uses the decode kernel (scale factored per group, MFMA
+ *   accumulation); larger M uses the prefill kernel (fp16 W_hat tiles in LDS,
+ *   MFMA).  Accumulation is fp32 in both; output is fp16 RNE.
+ * Accuracy: |y - y_ref| <= 2e-3 * sum_k |x_k * w_hat_k| + 1e-5 per output,
+ * y_ref the exact (fp64) product of the fp16 inputs. */
+exq_status exq_gemm(const void* x, int M, exq_layer_t layer, void* y, void* stream);
+
+/* Materialize W_hat^T: w_out device, fp16 [K][N] row-major (w_out[k*N + n]),
+ * bit-exact fp16_RNE((c - 2^(b-1)) * s).  Meant for testing and inspection. */
+exq_status exq_dequant(exq_layer_t layer, void* w_out, void* stream);
+
+/* ------------------------------------------------------- batched launches */
+
+/* Bind a list of independent linears into one launch (for a decode step:
+ * the pages' fused kernels cut launch overhead at small batch, per the
+ * ainews.cool exllamav3 article, section "technical deep dive").
+ *   count   number of linears, >= 1
+ *   layers  host array of handles (borrowed; must outlive the plan)
+ *   xs, ys  host arrays of device pointers, fp16 [M][K_i] and [M][N_i]
+ *   M       1..16, the same for every linear
+ * A plan owns a small device copy of these descriptors; buffers are bound at
+ * creation, like a captured graph.  exq_plan_run computes every y_i =
+ * x_i * W_i^T with the same numerics as exq_gemm, in one kernel launch.
+ * Outputs must not overlap any input or each other. */
+exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* const* xs,
+                           const void* const* ys, int M, exq_plan_t* out);
+exq_status exq_plan_run(exq_plan_t plan, void* stream);
+void exq_plan_destroy(exq_plan_t plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXQ_H */

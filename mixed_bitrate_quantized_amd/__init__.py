@@ -1,0 +1,228 @@
+"""Python binding of libexq: mixed-bitrate (EXL2-style) quantized linears on MI355X.
+
+Argument marshalling only.  Every step of the path -- packing, dequantization
+and the matmul -- runs in libexq (host C++ and gfx950 HIP kernels); PyTorch
+is used for device memory and streams.  The library is loaded from this
+directory; importing the package fails loudly when it is missing and cannot
+be built, and there is no fallback path.
+
+The C entry points keep their names (``exq_pack``, ``exq_layer_create``,
+``exq_gemm``, ...); see ``include/exq.h`` for argument meaning, layout,
+ownership and errors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libexq.so")
+GROUP = 128
+MAX_DECODE_M = 16
+
+EXQ_OK, EXQ_ERR_INVALID_ARG, EXQ_ERR_UNSUPPORTED, EXQ_ERR_HIP, EXQ_ERR_OOM = range(5)
+
+
+class ExqError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str):
+        super().__init__("%s failed: %s (%s)" % (what, _status_name(status), detail))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.exq_status_string.argtypes = [i32]
+    lib.exq_status_string.restype = ctypes.c_char_p
+    lib.exq_last_error.argtypes = []
+    lib.exq_last_error.restype = ctypes.c_char_p
+    lib.exq_packed_bytes.argtypes = [i32, i32, i32, vp]
+    lib.exq_packed_bytes.restype = u64
+    lib.exq_pack.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.exq_layer_create.argtypes = [i32, i32, i32, vp, vp, vp, ctypes.POINTER(vp)]
+    lib.exq_layer_destroy.argtypes = [vp]
+    lib.exq_layer_destroy.restype = None
+    lib.exq_gemm.argtypes = [vp, i32, vp, vp, vp]
+    lib.exq_dequant.argtypes = [vp, vp, vp]
+    lib.exq_plan_create.argtypes = [i32, vp, vp, vp, i32, ctypes.POINTER(vp)]
+    lib.exq_plan_run.argtypes = [vp, vp]
+    lib.exq_plan_destroy.argtypes = [vp]
+    lib.exq_plan_destroy.restype = None
+    for f in (lib.exq_pack, lib.exq_layer_create, lib.exq_gemm, lib.exq_dequant, lib.exq_plan_create,
+              lib.exq_plan_run):
+        f.restype = i32
+    return lib
+
+
+lib = _load()
+
+# Symbols include/exq.h declares (checked by the tests).
+EXPORTED = (
+    "exq_status_string", "exq_last_error", "exq_packed_bytes", "exq_pack", "exq_layer_create",
+    "exq_layer_destroy", "exq_gemm", "exq_dequant", "exq_plan_create", "exq_plan_run", "exq_plan_destroy",
+)
+
+
+def _status_name(s: int) -> str:
+    return lib.exq_status_string(s).decode()
+
+
+def _check(status: int, what: str):
+    if status != EXQ_OK:
+        raise ExqError(status, what, lib.exq_last_error().decode())
+
+
+def _np_ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _stream_ptr(stream) -> int | None:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+# ------------------------------------------------------------- entry points
+
+def exq_status_string(status: int) -> str:
+    return _status_name(status)
+
+
+def exq_packed_bytes(K: int, N: int, widths, group_size: int = GROUP) -> int:
+    w = np.ascontiguousarray(widths, dtype=np.uint8)
+    return int(lib.exq_packed_bytes(K, N, group_size, _np_ptr(w)))
+
+
+def exq_pack(W: np.ndarray, widths, group_size: int = GROUP):
+    """Host quantize + pack.  W fp32 [N][K] -> (qweight uint8 bytes, scales fp16 bits uint16 [G][N])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    w = np.ascontiguousarray(widths, dtype=np.uint8)
+    nbytes = exq_packed_bytes(K, N, w, group_size)
+    if nbytes == 0:
+        _check(lib.exq_pack(_np_ptr(W), K, N, group_size, _np_ptr(w), None, None), "exq_pack")
+    q = np.empty(nbytes, dtype=np.uint8)
+    s = np.empty((K // group_size, N), dtype=np.uint16)
+    _check(lib.exq_pack(_np_ptr(W), K, N, group_size, _np_ptr(w), _np_ptr(q), _np_ptr(s)), "exq_pack")
+    return q, s
+
+
+def exq_layer_create(K: int, N: int, widths, d_qweight: int, d_scales: int, group_size: int = GROUP) -> int:
+    w = np.ascontiguousarray(widths, dtype=np.uint8)
+    h = ctypes.c_void_p()
+    _check(lib.exq_layer_create(K, N, group_size, _np_ptr(w), d_qweight, d_scales, ctypes.byref(h)),
+           "exq_layer_create")
+    return h.value
+
+
+def exq_layer_destroy(handle: int) -> None:
+    lib.exq_layer_destroy(handle)
+
+
+def exq_gemm(x_ptr: int, M: int, handle: int, y_ptr: int, stream=None) -> None:
+    _check(lib.exq_gemm(x_ptr, M, handle, y_ptr, _stream_ptr(stream)), "exq_gemm")
+
+
+def exq_dequant(handle: int, w_ptr: int, stream=None) -> None:
+    _check(lib.exq_dequant(handle, w_ptr, _stream_ptr(stream)), "exq_dequant")
+
+
+def exq_plan_create(handles, x_ptrs, y_ptrs, M: int) -> int:
+    n = len(handles)
+    H = (ctypes.c_void_p * n)(*handles)
+    X = (ctypes.c_void_p * n)(*x_ptrs)
+    Y = (ctypes.c_void_p * n)(*y_ptrs)
+    p = ctypes.c_void_p()
+    _check(lib.exq_plan_create(n, H, X, Y, M, ctypes.byref(p)), "exq_plan_create")
+    return p.value
+
+
+def exq_plan_run(plan: int, stream=None) -> None:
+    _check(lib.exq_plan_run(plan, _stream_ptr(stream)), "exq_plan_run")
+
+
+def exq_plan_destroy(plan: int) -> None:
+    lib.exq_plan_destroy(plan)
+
+
+# ------------------------------------------------------------ conveniences
+
+class Layer:
+    """A packed layer resident on the GPU: owns its torch buffers and the handle."""
+
+    def __init__(self, K: int, N: int, widths, qweight: np.ndarray, scales: np.ndarray, device="cuda"):
+        import torch
+        self.K, self.N = K, N
+        self.widths = np.ascontiguousarray(widths, dtype=np.uint8)
+        self.qweight = torch.from_numpy(np.ascontiguousarray(qweight)).to(device)
+        self.scales = torch.from_numpy(np.ascontiguousarray(scales).view(np.int16)).to(device)
+        self.handle = exq_layer_create(K, N, self.widths, self.qweight.data_ptr(), self.scales.data_ptr())
+
+    @classmethod
+    def from_weight(cls, W: np.ndarray, widths, device="cuda"):
+        q, s = exq_pack(W, widths)
+        N, K = W.shape
+        return cls(K, N, widths, q, s, device)
+
+    @property
+    def packed_bytes(self) -> int:
+        return int(self.qweight.numel())
+
+    def gemm(self, x, out=None, stream=None):
+        """x: torch fp16 [M][K] on the GPU -> y fp16 [M][N]."""
+        import torch
+        assert x.dtype == torch.float16 and x.is_contiguous() and x.shape[-1] == self.K
+        M = x.shape[0]
+        if out is None:
+            out = torch.empty((M, self.N), dtype=torch.float16, device=x.device)
+        exq_gemm(x.data_ptr(), M, self.handle, out.data_ptr(), stream)
+        return out
+
+    def dequant(self, stream=None):
+        import torch
+        w = torch.empty((self.K, self.N), dtype=torch.float16, device=self.qweight.device)
+        exq_dequant(self.handle, w.data_ptr(), stream)
+        return w
+
+    def close(self):
+        if self.handle:
+            exq_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Plan:
+    """Independent linears bound to fixed x/y buffers, run as one launch."""
+
+    def __init__(self, layers, xs, ys, M: int):
+        self.layers, self.xs, self.ys = list(layers), list(xs), list(ys)  # keep buffers alive
+        self.handle = exq_plan_create([l.handle for l in self.layers], [x.data_ptr() for x in self.xs],
+                                      [y.data_ptr() for y in self.ys], M)
+
+    def run(self, stream=None):
+        exq_plan_run(self.handle, stream)
+
+    def close(self):
+        if self.handle:
+            exq_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

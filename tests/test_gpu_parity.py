@@ -1,0 +1,202 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C-ABI.
+
+Bar: packed bytes, scales and dequantized weights bit-exact; matmul outputs
+within |y - y_ref| <= 2e-3 * sum|x*w| + 1e-5 per output; special cases
+(zero, one-hot, integer closed form, power-of-two scales, doubling) bit-exact.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_helpers import assert_within, note, sample_cols, to_dev, y_to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def exq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixed_bitrate_quantized_amd as m
+    return m
+
+
+def make_layer(exq, W, widths):
+    q, s = exq.exq_pack(W, widths)
+    codes, s_ref, q_ref = oracle.reference_layer(W, widths)
+    np.testing.assert_array_equal(s, s_ref)
+    np.testing.assert_array_equal(q, q_ref)
+    N, K = W.shape
+    return exq.Layer(K, N, widths, q, s), codes, s_ref, q_ref
+
+
+def full_check(exq, W, widths, Ms, tag):
+    N, K = W.shape
+    layer, codes, s_ref, q_ref = make_layer(exq, W, widths)
+    note("%s dequant K=%d N=%d" % (tag, K, N))
+    wd = layer.dequant().cpu().numpy().view(np.uint16)
+    w_ref = oracle.dequant(codes, s_ref, widths)
+    np.testing.assert_array_equal(wd, w_ref)
+    worst = 0.0
+    for M in Ms:
+        x = synth.activations(synth.seed_for(tag, "x", M), M, K)
+        note("%s gemm M=%d" % (tag, M))
+        y = y_to_np(layer.gemm(to_dev(x)))
+        y_ref, bnd = oracle.gemm(x, w_ref)
+        worst = max(worst, assert_within(y, y_ref, bnd, "%s M=%d" % (tag, M)))
+    layer.close()
+    return worst
+
+
+# ------------------------------------------------------------ small shapes
+
+SMALL_WIDTHS = [2, 3, 4, 5, 6, 8, 3]
+
+
+def test_small_layer_every_width_ragged_M(exq):
+    W = synth.weight(synth.seed_for("small"), 192, 128 * len(SMALL_WIDTHS))
+    full_check(exq, W, SMALL_WIDTHS, [1, 2, 3, 4, 5, 7, 8, 9, 12, 13, 16, 17, 33], "small")
+
+
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 6, 8])
+def test_single_group_each_width(exq, b):
+    W = synth.weight(synth.seed_for("single", b), 64, 128)
+    full_check(exq, W, [b], [1, 6], "single-b%d" % b)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_forced_split_counts(exq, splits, monkeypatch):
+    monkeypatch.setenv("EXQ_FORCE_SPLITS", str(splits))
+    widths = [2, 2, 3, 8, 2, 4, 2, 6, 5, 2, 3, 2, 2, 3, 2, 2, 2, 2, 3, 2]
+    W = synth.weight(synth.seed_for("splits"), 320, 128 * len(widths))
+    full_check(exq, W, widths, [1, 4, 16], "splits%d" % splits)
+
+
+def test_zero_and_one_hot_and_doubling(exq):
+    widths = [3, 5, 2, 8]
+    W = synth.weight(synth.seed_for("special"), 128, 512)
+    layer, codes, s_ref, q_ref = make_layer(exq, W, widths)
+    w_ref = oracle.dequant(codes, s_ref, widths)
+    note("special: zero input")
+    for M in (1, 3, 16, 20):
+        y = y_to_np(layer.gemm(to_dev(np.zeros((M, 512), dtype=np.float16))))
+        assert np.all(y == 0)
+    note("special: one-hot rows")
+    ks = np.array([0, 1, 127, 128, 200, 255, 256, 300, 383, 384, 450, 511, 5, 77, 131, 260])
+    x = np.zeros((16, 512), dtype=np.float16)
+    x[np.arange(16), ks] = 1.0
+    y = y_to_np(layer.gemm(to_dev(x)))
+    np.testing.assert_array_equal(y.view(np.uint16), w_ref[ks])
+    note("special: y(2x) == 2 y(x)")
+    for M in (1, 7):
+        x = synth.activations(synth.seed_for("dbl", M), M, 512)
+        y1 = y_to_np(layer.gemm(to_dev(x)))
+        y2 = y_to_np(layer.gemm(to_dev((x.astype(np.float32) * 2).astype(np.float16))))
+        # exact where y is an fp16 normal (fp16 rounding commutes with doubling there)
+        normal = np.abs(y1.astype(np.float32)) >= 2.0 ** -13
+        np.testing.assert_array_equal(y2[normal], (y1[normal].astype(np.float32) * 2).astype(np.float16))
+        assert np.all(np.abs(y2[~normal].astype(np.float64) - 2 * y1[~normal].astype(np.float64)) <= 2.0 ** -24)
+    layer.close()
+
+
+def test_integer_closed_form_all_8bit_unit_scale(exq):
+    """All 8-bit, every scale exactly 1, x in {-1,0,1}: y is the integer matmul, bit-exact."""
+    rng = np.random.default_rng(17)
+    K, N = 384, 128
+    Wi = rng.integers(-127, 128, size=(N, K))
+    Wi[:, ::128] = 127                      # max |w| = 127 in every (group, column): scale 1
+    W = Wi.astype(np.float32)
+    layer, codes, s_ref, _ = make_layer(exq, W, [8, 8, 8])
+    assert np.all(s_ref == 0x3C00)
+    for M in (1, 4, 16, 40):
+        x = rng.integers(-1, 2, size=(M, K)).astype(np.float16)
+        note("closed form M=%d" % M)
+        y = y_to_np(layer.gemm(to_dev(x)))
+        ref = (x.astype(np.int64) @ Wi.T).astype(np.float16)
+        np.testing.assert_array_equal(y, ref)
+    layer.close()
+
+
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 6, 8])
+def test_power_of_two_scales_exact(exq, b):
+    rng = np.random.default_rng(100 + b)
+    qmax = (1 << (b - 1)) - 1
+    K, N = 256, 64
+    e = rng.integers(-6, 3, size=(N, 2))
+    Q = rng.integers(-qmax, qmax + 1, size=(N, K))
+    Q[:, 0] = qmax
+    Q[:, 128] = -qmax
+    W = (Q * np.repeat(2.0 ** e, 128, axis=1)).astype(np.float32)
+    layer, _, s_ref, _ = make_layer(exq, W, [b, b])
+    np.testing.assert_array_equal(s_ref.view(np.float16).astype(np.float64), (2.0 ** e).T)
+    for M in (1, 5, 30):
+        x = rng.integers(-2, 3, size=(M, K)).astype(np.float16)
+        note("pow2 b=%d M=%d" % (b, M))
+        y = y_to_np(layer.gemm(to_dev(x)))
+        ref = x.astype(np.float64) @ W.astype(np.float64).T
+        np.testing.assert_array_equal(y, ref.astype(np.float16))
+    layer.close()
+
+
+def test_determinism_and_guard_bands(exq):
+    widths = [2, 3, 2, 8, 2, 2, 4, 2]
+    K, N = 1024, 256
+    W = synth.weight(synth.seed_for("guard"), N, K)
+    layer, *_ = make_layer(exq, W, widths)
+    for M in (1, 16, 24):
+        x = to_dev(synth.activations(synth.seed_for("guard-x", M), M, K))
+        pad = 4096
+        buf = torch.full((M * N + 2 * pad,), -12345, dtype=torch.int16, device="cuda")
+        out = buf[pad:pad + M * N].view(torch.float16).view(M, N)
+        note("guard M=%d" % M)
+        layer.gemm(x, out=out)
+        first = y_to_np(out).copy()
+        layer.gemm(x, out=out)
+        np.testing.assert_array_equal(y_to_np(out), first)
+        b = buf.cpu().numpy()
+        assert np.all(b[:pad] == -12345) and np.all(b[pad + M * N:] == -12345)
+    layer.close()
+
+
+def test_plan_matches_individual_calls(exq):
+    specs = [(256, 64, [2, 3]), (512, 192, [8, 2, 6, 5]), (1024, 128, [2] * 7 + [4]), (384, 320, [3, 3, 4])]
+    layers, xs, ys, singles = [], [], [], []
+    for i, (K, N, widths) in enumerate(specs):
+        W = synth.weight(synth.seed_for("plan", i), N, K)
+        layer, *_ = make_layer(exq, W, widths)
+        layers.append(layer)
+    for M in (1, 3, 16):
+        xs = [to_dev(synth.activations(synth.seed_for("plan-x", i, M), M, l.K)) for i, l in enumerate(layers)]
+        ys = [torch.empty((M, l.N), dtype=torch.float16, device="cuda") for l in layers]
+        note("plan M=%d" % M)
+        plan = exq.Plan(layers, xs, ys, M)
+        plan.run()
+        got = [y_to_np(y) for y in ys]
+        for l, x, g in zip(layers, xs, got):
+            np.testing.assert_array_equal(g, y_to_np(l.gemm(x)))
+        plan.run()   # split-K counters are left at zero: a second run is identical
+        for y, g in zip(ys, got):
+            np.testing.assert_array_equal(y_to_np(y), g)
+        plan.close()
+    for l in layers:
+        l.close()
+
+
+def test_runtime_errors_on_device(exq):
+    W = synth.weight(synth.seed_for("err"), 64, 256)
+    layer, *_ = make_layer(exq, W, [2, 4])
+    x = to_dev(np.zeros((2, 256), dtype=np.float16))
+    with pytest.raises(exq.ExqError) as ei:
+        exq.exq_gemm(x.data_ptr(), 0, layer.handle, x.data_ptr() + 4096)
+    assert ei.value.status == exq.EXQ_ERR_INVALID_ARG
+    with pytest.raises(exq.ExqError) as ei:   # y overlaps x
+        exq.exq_gemm(x.data_ptr(), 2, layer.handle, x.data_ptr() + 64)
+    assert ei.value.status == exq.EXQ_ERR_INVALID_ARG
+    with pytest.raises(exq.ExqError):
+        exq.exq_gemm(x.data_ptr() + 2, 1, layer.handle, x.data_ptr() + 4096)
+    layer.close()

@@ -1,0 +1,86 @@
+"""The five synthetic workloads at full size on the GPU, against the oracle.
+
+Packed bytes, scales and W_hat are compared bit for bit (W_hat for every
+linear of configs 1-4); outputs are compared on seeded samples of columns
+(and, at M = 2048, of rows) that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import workloads
+from tests.gpu_helpers import assert_within, note, sample_cols, to_dev, y_to_np
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def exq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixed_bitrate_quantized_amd as m
+    return m
+
+
+def check_linear(exq, spec, Ms, ncols=256, nrows=None, dequant=True):
+    note("cfg%d %s K=%d N=%d: generate + pack" % (spec.config, spec.name, spec.K, spec.N))
+    W = workloads.make_weight(spec)
+    widths = workloads.make_widths(spec, W)
+    q, s = exq.exq_pack(W, widths)
+    codes, s_ref, q_ref = oracle.reference_layer(W, widths)
+    np.testing.assert_array_equal(s, s_ref)
+    np.testing.assert_array_equal(q, q_ref)
+    del W
+    layer = exq.Layer(spec.K, spec.N, widths, q, s)
+    if dequant:
+        note("cfg%d %s dequant" % (spec.config, spec.name))
+        wd = layer.dequant().cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(wd, oracle.dequant(codes, s_ref, widths))
+        del wd
+    del codes
+    cols = sample_cols(spec.N, ncols, spec.w_seed() & 0xFFFF)
+    worst = 0.0
+    for M in Ms:
+        x = workloads.make_x(spec, M)
+        note("cfg%d %s gemm M=%d" % (spec.config, spec.name, M))
+        y = y_to_np(layer.gemm(to_dev(x)))
+        rows = np.arange(M)
+        if nrows is not None and M > nrows:
+            rng = np.random.default_rng(M)
+            rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, nrows, replace=False)]))
+        y_ref, bnd = oracle.gemm_packed_cols(x[rows], q_ref, s_ref, widths, spec.K, spec.N, cols)
+        worst = max(worst, assert_within(y[np.ix_(rows, cols)], y_ref, bnd, "cfg%d %s M=%d" % (spec.config, spec.name, M)))
+    layer.close()
+    return worst
+
+
+def test_cfg1_uniform_4bit_4096(exq):
+    spec = workloads.linears(1)[0]
+    check_linear(exq, spec, workloads.M_VALUES[1], ncols=spec.N)
+
+
+def test_cfg2_mixed_8192(exq):
+    spec = workloads.linears(2)[0]
+    check_linear(exq, spec, workloads.M_VALUES[2], ncols=512)
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_cfg3_block_linear(exq, idx):
+    spec = workloads.linears(3)[idx]
+    check_linear(exq, spec, workloads.M_VALUES[3], ncols=256)
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_cfg4_prefill_linear(exq, idx):
+    spec = workloads.linears(4)[idx]
+    check_linear(exq, spec, workloads.M_VALUES[4], ncols=96, nrows=32)
+
+
+CFG5_SAMPLE = (0, 6, 37 * 7 + 4, 79 * 7 + 1)
+
+
+@pytest.mark.parametrize("idx", CFG5_SAMPLE)
+def test_cfg5_stack_sample(exq, idx):
+    spec = workloads.linears(5)[idx]
+    check_linear(exq, spec, workloads.M_VALUES[5], ncols=128, dequant=False)

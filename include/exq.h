@@ -99,9 +99,11 @@ exq_status exq_pack(const float* W, int K, int N, int group_size, const uint8_t*
  *   widths_host host, uint8 [K/128]; copied, the caller may free it
  *   d_qweight   device, 16-byte aligned EXQ1 words (borrowed: must outlive the handle)
  *   d_scales    device, 16-byte aligned fp16 [G][N] (borrowed)
- * The handle owns small device metadata and a split-K workspace; it may be
- * used by one stream at a time.  Errors: INVALID_ARG, UNSUPPORTED
- * (group_size != 128), OOM, HIP. */
+ * The handle owns a few kilobytes of device metadata (the per-group offsets
+ * and the width-sorted visiting order); it holds no scratch state, so any
+ * number of streams may use it at once.  Errors: INVALID_ARG, UNSUPPORTED
+ * (group_size != 128, or K so large that one workgroup's activation sums do
+ * not fit in LDS), OOM, HIP. */
 exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_host,
                             const void* d_qweight, const void* d_scales, exq_layer_t* out);
 
@@ -134,7 +136,9 @@ exq_status exq_dequant(exq_layer_t layer, void* w_out, void* stream);
  *   M       1..16, the same for every linear
  * A plan owns a small device copy of these descriptors; buffers are bound at
  * creation, like a captured graph.  exq_plan_run computes every y_i =
- * x_i * W_i^T with the same numerics as exq_gemm, in one kernel launch.
+ * x_i * W_i^T in one kernel launch, deterministically and to the same
+ * accuracy bound as exq_gemm (its tiling, hence its summation order, may
+ * differ from a single exq_gemm call).
  * Outputs must not overlap any input or each other. */
 exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* const* xs,
                            const void* const* ys, int M, exq_plan_t* out);

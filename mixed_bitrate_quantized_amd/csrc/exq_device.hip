@@ -2,23 +2,25 @@
 // plan management.  The prefill GEMM lives in exq_prefill.hip.
 //
 // Decode design (M <= 16, HBM-bound):
-//   * one lane per output column, 64 columns per wave, all four waves of a
-//     workgroup on the same 64 columns but on different byte-balanced runs of
-//     K groups; the column's b_g 16-byte words of a group arrive as b_g
-//     coalesced 1 KB wave loads;
-//   * a code field is masked in place into the low bits of an fp16 half, which
-//     then *is* the fp16 value c * 2^(o-24) (a subnormal): one AND per two
-//     weights, no conversion, no zero-point subtraction per weight;
+//   * a workgroup owns 16 output columns over the whole of K; its 8 waves
+//     share the groups, pre-sorted by width and cut into byte-balanced
+//     chunks, so a wave streams one or two runs of equal-width groups and its
+//     software pipeline waits on compile-time load counts;
+//   * lane l handles column l % 16 and K-quarter q = l / 16 of every group:
+//     it loads exactly the 4*b bytes of EXQ1 storage that hold codes
+//     [32q, 32q+32) of its column, and the 16 lanes of a quarter read
+//     contiguous 256-byte runs;
+//   * a code field is masked in place into the low bits of an fp16 half,
+//     which then *is* the fp16 value c * 2^(o-24) (a subnormal): one AND per
+//     two weights, no conversion and no zero-point subtraction per weight;
 //   * the multiply-accumulate runs on the matrix cores with
-//     v_mfma_f32_4x4x4_16b_f16: 16 blocks of 4 columns, the activation operand
-//     of one block broadcast to all 16 (cbsz = 4), so the activations of a
-//     whole group fit in four VGPRs per row block;
-//   * per group, the per-offset partial sums are rescaled by 2^(24-o), the
-//     zero point is removed once with the group's activation sum (computed per
-//     workgroup into LDS), and the fp16 scale is applied in fp32:
-//       y += s * (sum_k x_k c_k - 2^(b-1) sum_k x_k);
-//   * waves reduce through LDS in fixed order; when K is split across
-//     workgroups the last one to finish adds the fp32 partials in split order.
+//     v_mfma_f32_4x4x4_16b_f16; each 16-lane quarter is a set of four 4x4
+//     blocks that shares one activation block (cbsz = 2), read from LDS;
+//   * per group the per-offset partial sums are rescaled by 2^(24-o), the
+//     zero point is removed once with the quarter's activation sum and the
+//     fp16 scale is applied in fp32:  y += s * (sum x*c - 2^(b-1) * sum x);
+//   * quarters and waves are reduced in a fixed order: no atomics, the result
+//     is deterministic.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -41,13 +43,22 @@ struct LinearDev {
     const uint8_t* qweight;   // EXQ1 words
     const uint16_t* scales;   // fp16 [G][N]
     const uint32_t* meta;     // [G]: (P_g << 4) | b_g
-    const uint16_t* bounds;   // [S*kWaves + 1] group cut points
+    const uint32_t* order;    // [G]: g | (P_g << 16), sorted by width
+    const uint16_t* bounds;   // [kWaves + 1] wave chunks of `order`
+    const uint16_t* runs;     // [kWaves][6] groups of width 2,3,4,5,6,8 per chunk
     const uint16_t* x;        // fp16 [M][K]
     uint16_t* y;              // fp16 [M][N]
-    float* partial;           // fp32 [S][M][N] split-K partial sums (S > 1)
-    uint32_t* counters;       // [N/64] arrival counters (S > 1), zero between launches
-    int K, N, G, S, tiles, wg_begin;
+    int K, N, G, tiles, wg_begin;
 };
+
+// Global-address-space views: loads through them are global_load (vmcnt
+// only), never flat_load, whose lgkmcnt coupling would make every LDS read
+// wait for all weight loads in flight.
+#define EXQ_GLOBAL __attribute__((address_space(1)))
+template <class T> __device__ __forceinline__ const EXQ_GLOBAL T* gptr(const void* p) {
+    return (const EXQ_GLOBAL T*)p;
+}
+template <class T> __device__ __forceinline__ EXQ_GLOBAL T* gptr_w(void* p) { return (EXQ_GLOBAL T*)p; }
 
 template <int I> using IC = std::integral_constant<int, I>;
 
@@ -72,17 +83,24 @@ __device__ __forceinline__ h4 as_h4(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(h4, v);
 }
 
-// Decoder unit U of a width-B group (U in [0,32)): returns two dwords whose
-// 16-bit halves hold codes 4U, 4U+1 (b0) and 4U+2, 4U+3 (b1), each code at bit
-// offset o = p0*(U % per) of its half and every other bit clear.  Read as fp16
-// the halves are exactly c * 2^(o-24).  The bit positions follow the EXQ1
-// layout of include/exq.h.
-template <int B, int U>
-__device__ __forceinline__ void unit_pair(const uint32_t* D, uint32_t& b0, uint32_t& b1) {
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Decoder unit U of a width-B group, on the dwords of NQ consecutive
+// K-quarters (NQ = 4: the whole group, U in [0, 32); NQ = 1: quarter q, U in
+// [0, 8) covering codes 32q + 4U ..).  Q holds the NQ*p0 plane-0 dwords then
+// the NQ*p1 plane-1 dwords.  Returns two dwords whose 16-bit
+// halves hold codes 4U, 4U+1 (b0) and 4U+2, 4U+3 (b1), each at bit offset
+// o = p0 * (U % per) of its half, every other bit clear.  Read as fp16 the
+// halves are exactly c * 2^(o-24).  Bit positions follow the EXQ1 layout
+// (include/exq.h); the quarter split keeps dword-local positions unchanged.
+template <int B, int U, int NQ = 1>
+__device__ __forceinline__ void unit_pair(const uint32_t* Q, uint32_t& b0, uint32_t& b1) {
     using T = Width<B>;
     constexpr int d = U / T::per, t = U % T::per, o = T::p0 * t;
     constexpr uint32_t mlo = (((1u << T::p0) - 1u) * 0x00010001u) << o;
-    const uint32_t lo0 = D[d], lo1 = D[d] >> 8;
+    const uint32_t lo0 = Q[d], lo1 = Q[d] >> 8;
     if constexpr (T::p1 == 0) {
         b0 = lo0 & mlo;
         b1 = lo1 & mlo;
@@ -92,7 +110,7 @@ __device__ __forceinline__ void unit_pair(const uint32_t* D, uint32_t& b0, uint3
         constexpr int sh0 = T::p0 - T::p1 * delta;      // left shift, high fields of codes 4U, 4U+1
         constexpr int sh1 = T::p1 * delta + 8 - T::p0;  // right shift, codes 4U+2, 4U+3
         static_assert(sh0 > 0 && sh1 > 0, "plane-1 alignment");
-        const uint32_t H = D[4 * T::p0 + h];
+        const uint32_t H = Q[NQ * T::p0 + h];
         b0 = (lo0 & mlo) | ((H << sh0) & mhi);
         b1 = (lo1 & mlo) | ((H >> sh1) & mhi);
     }
@@ -103,240 +121,313 @@ template <int B> __device__ constexpr float class_factor(int t) {
     return (float)(1u << (24 - Width<B>::p0 * t));
 }
 
-// ----------------------------------------------------------------- decode
-
-template <int MB>
-__device__ __forceinline__ void load_group(const LinearDev& L, int g, int M, int n, int lane,
-                                           uint32_t (&D)[32], u4v (&X)[MB], uint16_t& s, int& b) {
-    const uint32_t meta = L.meta[g];
-    b = (int)(meta & 15u);
-    const size_t P = meta >> 4;
-    const u4v* base = reinterpret_cast<const u4v*>(L.qweight) + ((size_t)L.N * P + (size_t)n);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (j < b) {
-            u4v v = __builtin_nontemporal_load(base + (size_t)j * (size_t)L.N);
-            D[4 * j + 0] = v[0];
-            D[4 * j + 1] = v[1];
-            D[4 * j + 2] = v[2];
-            D[4 * j + 3] = v[3];
-        }
-    }
-    s = L.scales[(size_t)g * L.N + n];
-    const int a = lane >> 2, i = lane & 3;
-#pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-        const int row = min(4 * rb + i, M - 1);
-        X[rb] = *reinterpret_cast<const u4v*>(L.x + (size_t)row * L.K + (size_t)g * kGroup + 8 * a);
+// Loads the B dwords of quarter q of column n, group at word offset P.
+// Plane p occupies column-local dwords [m0 + q*p, m0 + (q+1)*p): a p-dword
+// piece of one 16-byte word for p <= 4, two whole words for p = 8.
+template <int P_DW>
+__device__ __forceinline__ void load_piece(const uint8_t* col, size_t N, int m, uint32_t* dst) {
+    const uint8_t* a = col + 16 * (size_t)(m >> 2) * N + 4 * (m & 3);
+    if constexpr (P_DW == 1) {
+        dst[0] = __builtin_nontemporal_load(gptr<uint32_t>(a));
+    } else if constexpr (P_DW == 2) {
+        const u2v v = __builtin_nontemporal_load(gptr<u2v>(a));
+        dst[0] = v[0];
+        dst[1] = v[1];
+    } else {
+        const u4v v = __builtin_nontemporal_load(gptr<u4v>(a));
+        dst[0] = v[0];
+        dst[1] = v[1];
+        dst[2] = v[2];
+        dst[3] = v[3];
     }
 }
 
-template <int B, int MB>
-__device__ __forceinline__ void group_compute(const uint32_t (&D)[32], const u4v (&X)[MB], uint16_t s16,
-                                              const float* xs, int xs_stride, int M, float (&yacc)[MB][4]) {
+template <int B>
+__device__ __forceinline__ void load_quarter(const uint8_t* qw, size_t N, size_t P, size_t n, int q,
+                                             uint32_t (&Q)[B]) {
+    using T = Width<B>;
+    const uint8_t* col = qw + 16 * (N * P + n);
+    if constexpr (T::p0 == 8) {
+        load_piece<4>(col, N, 8 * q, Q);
+        load_piece<4>(col, N, 8 * q + 4, Q + 4);
+    } else {
+        load_piece<T::p0>(col, N, T::p0 * q, Q);
+    }
+    if constexpr (T::p1 > 0) load_piece<T::p1>(col, N, 4 * T::p0 + T::p1 * q, Q + T::p0);
+}
+
+// All B words of column n of the group at word offset P (one 1 KB wave load each).
+template <int B>
+__device__ __forceinline__ void load_group_words(const uint8_t* qw, size_t N, size_t P, size_t n,
+                                                 uint32_t (&D)[4 * B]) {
+    const EXQ_GLOBAL u4v* base = gptr<u4v>(qw) + (N * P + n);
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        const u4v v = __builtin_nontemporal_load(base + (size_t)j * N);
+        D[4 * j + 0] = v[0];
+        D[4 * j + 1] = v[1];
+        D[4 * j + 2] = v[2];
+        D[4 * j + 3] = v[3];
+    }
+}
+
+struct DecodeCtx {
+    int M, lane, q, n;
+};
+
+template <int TC> struct Tile {
+    static constexpr int NQ = TC == 64 ? 4 : 1;     // K-quarters of a group per lane
+    static constexpr int UNITS = 8 * NQ;            // decoder units per lane per group
+    static constexpr int CBSZ = TC == 64 ? 4 : 2;   // 16 or 4 blocks share one activation block
+};
+
+// Activation operand of row block rb.  TC = 64: lane (a = l/4, i = l%4) holds
+// x[4rb + i][128g + 8a .. +8).  TC = 16: lane (q, a = (l%16)/4, i) holds
+// x[4rb + i][128g + 32q + 8a .. +8).  Rows past M repeat row M-1 (unused).
+template <int TC>
+__device__ __forceinline__ u4v load_act(const LinearDev& L, const DecodeCtx& c, int g, int rb) {
+    const int a = (TC == 64 ? c.lane : (c.lane & 15)) >> 2, i = c.lane & 3;
+    const int row = min(4 * rb + i, c.M - 1);
+    const size_t off = (size_t)row * L.K + (size_t)g * kGroup + (TC == 64 ? 0 : 32 * c.q) + 8 * a;
+    return *gptr<u4v>(L.x + off);
+}
+
+// Sum of the activations a lane's column sees in this group (TC = 64: the
+// whole group; TC = 16: its quarter), for row 4rb + r: the 8 values of each
+// operand lane are summed with dot2 against ones, then the lanes holding the
+// same row are combined by xor-shuffles in a fixed order.  Every lane ends
+// with the sum for row (its lane % 4); the row-r value is then broadcast.
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// fp16 pair view of a dword.  The argument is a plain scalar on purpose:
+// __builtin_bit_cast applied directly to an ext_vector element (x[i]) has
+// been seen to read element 0 whatever i is.
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+
+template <int TC>
+__device__ __forceinline__ float act_sum_lane(const u4v X) {
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    float v = __builtin_amdgcn_fdot2(as_h2(X[0]), one, 0.0f, false);
+    v = __builtin_amdgcn_fdot2(as_h2(X[1]), one, v, false);
+    v = __builtin_amdgcn_fdot2(as_h2(X[2]), one, v, false);
+    v = __builtin_amdgcn_fdot2(as_h2(X[3]), one, v, false);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    if constexpr (TC == 64) {
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+    }
+    return v;
+}
+
+template <int TC>
+__device__ __forceinline__ float act_sum_row(float lane_sum, const DecodeCtx& c, int r) {
+    if constexpr (TC == 64) return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), r));
+    else return __shfl(lane_sum, 16 * c.q + r);
+}
+
+template <int B, int MB, int TC, bool M1>
+__device__ __forceinline__ void group_compute(const DecodeCtx& c, const uint32_t (&Q)[B * Tile<TC>::NQ],
+                                              const u4v (&X)[MB], uint16_t s16, float (&yacc)[MB][4]) {
+    using TT = Tile<TC>;
     constexpr int C = Width<B>::per;
     f4 acc[C][MB];
 #pragma unroll
     for (int t = 0; t < C; ++t)
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) acc[t][rb] = f4{0.f, 0.f, 0.f, 0.f};
-    static_for<0, 32>([&](auto UC) {
+    static_for<0, TT::UNITS>([&](auto UC) {
         constexpr int U = decltype(UC)::value;
         constexpr int t = U % C;
         uint32_t b0, b1;
-        unit_pair<B, U>(D, b0, b1);
+        unit_pair<B, U, TT::NQ>(Q, b0, b1);
         const h4 bv = as_h4(b0, b1);
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) {
             const h4 av = (U & 1) ? as_h4(X[rb][2], X[rb][3]) : as_h4(X[rb][0], X[rb][1]);
-            acc[t][rb] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, acc[t][rb], 4, U >> 1, 0);
+            acc[t][rb] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, acc[t][rb], TT::CBSZ, U >> 1, 0);
         }
     });
     const float s = (float)__builtin_bit_cast(_Float16, s16);
     constexpr float z = (float)(1 << (B - 1));
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb)
+    for (int rb = 0; rb < MB; ++rb) {
+        const float xl = act_sum_lane<TC>(X[rb]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (4 * rb + r < M) {
+        for (int r = 0; r < (M1 ? 1 : 4); ++r) {
+            if (M1 || 4 * rb + r < c.M) {
                 float tv = acc[0][rb][r] * class_factor<B>(0);
 #pragma unroll
                 for (int t = 1; t < C; ++t) tv = __builtin_fmaf(acc[t][rb][r], class_factor<B>(t), tv);
-                tv = __builtin_fmaf(-z, xs[(4 * rb + r) * xs_stride], tv);
+                tv = __builtin_fmaf(-z, act_sum_row<TC>(xl, c, r), tv);
                 yacc[rb][r] = __builtin_fmaf(s, tv, yacc[rb][r]);
             }
         }
-}
-
-template <int MB>
-__device__ __forceinline__ void group_dispatch(int b, const uint32_t (&D)[32], const u4v (&X)[MB], uint16_t s,
-                                               const float* xs, int xs_stride, int M, float (&yacc)[MB][4]) {
-    switch (b) {
-        case 2: group_compute<2, MB>(D, X, s, xs, xs_stride, M, yacc); break;
-        case 3: group_compute<3, MB>(D, X, s, xs, xs_stride, M, yacc); break;
-        case 4: group_compute<4, MB>(D, X, s, xs, xs_stride, M, yacc); break;
-        case 5: group_compute<5, MB>(D, X, s, xs, xs_stride, M, yacc); break;
-        case 6: group_compute<6, MB>(D, X, s, xs, xs_stride, M, yacc); break;
-        default: group_compute<8, MB>(D, X, s, xs, xs_stride, M, yacc); break;
     }
 }
 
-__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
-    return __builtin_bit_cast(uint16_t, (_Float16)v);
+template <int B, int TC> struct Depth {
+    // groups in flight per wave (the current one included)
+    static constexpr int value = TC == 64 ? ((B <= 2) ? 4 : (B <= 4 ? 3 : 2)) : ((B <= 3) ? 6 : (B <= 6 ? 4 : 3));
+};
+
+// A run of `cnt` width-B groups (entries ord[0..cnt)), pipelined DEPTH deep:
+// while group i is computed, groups i+1 .. i+DEPTH-1 are in flight.  Every
+// step issues exactly one group's loads -- weights, scale, activation
+// operands, in that order -- with the index clamped at the end of the run,
+// so each wait is a compile-time count.
+template <int B, int MB, int TC, bool M1>
+__device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c, const uint32_t* ord, int cnt,
+                                          float (&yacc)[MB][4]) {
+    constexpr int DEPTH = Depth<B, TC>::value;
+    constexpr int NDW = B * Tile<TC>::NQ;
+    uint32_t Q[DEPTH][NDW];
+    u4v X[DEPTH][MB];
+    uint16_t S[DEPTH];
+    const EXQ_GLOBAL uint32_t* og = gptr<uint32_t>(ord);
+    auto issue = [&](uint32_t e, uint32_t (&Qd)[NDW], u4v (&Xd)[MB], uint16_t& Sd) {
+        const int g = (int)(e & 0xFFFFu);
+        if constexpr (TC == 64) load_group_words<B>(L.qweight, (size_t)L.N, (size_t)(e >> 16), (size_t)c.n, Qd);
+        else load_quarter<B>(L.qweight, (size_t)L.N, (size_t)(e >> 16), (size_t)c.n, c.q, Qd);
+        Sd = *gptr<uint16_t>(L.scales + (size_t)g * L.N + c.n);
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) Xd[rb] = load_act<TC>(L, c, g, rb);
+    };
+    static_for<0, DEPTH - 1>([&](auto KC) {
+        constexpr int k = decltype(KC)::value;
+        issue(og[min(k, cnt - 1)], Q[k], X[k], S[k]);
+    });
+    for (int i = 0; i < cnt; i += DEPTH) {
+        bool done = false;
+        static_for<0, DEPTH>([&](auto KC) {
+            constexpr int k = decltype(KC)::value;
+            constexpr int nk = (k + DEPTH - 1) % DEPTH;
+            if (done || i + k >= cnt) {
+                done = true;
+                return;
+            }
+            issue(og[min(i + k + DEPTH - 1, cnt - 1)], Q[nk], X[nk], S[nk]);
+            group_compute<B, MB, TC, M1>(c, Q[k], X[k], S[k], yacc);
+        });
+    }
 }
 
-// One workgroup of the decode GEMV: 64 columns, one split of K.
-template <int MB>
-__device__ __forceinline__ void decode_wg(const LinearDev& L, int local, int M, float* lds) {
-    const int tile = local % L.tiles, split = local / L.tiles;
+// One decode workgroup: TC columns, all of K, kWaves waves.  No prologue:
+// every wave starts streaming at once and only the final reduction is shared.
+template <int MB, int TC, bool M1>
+__device__ __forceinline__ void decode_wg(const LinearDev& L, int tile, int M, float* red) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = tile * kTileCols + lane;
-    const int g0 = L.bounds[split * kWaves], g1 = L.bounds[split * kWaves + kWaves];
-    const int gs = g1 - g0;
-    float* xsum = lds;                       // [M][gs]
-    float* red = lds + ((M * gs + 3) & ~3);  // [kWaves][M][64]
+    DecodeCtx c;
+    c.M = M;
+    c.lane = lane;
+    c.q = TC == 64 ? 0 : lane >> 4;
+    c.n = tile * TC + (TC == 64 ? lane : (lane & 15));
 
-    // Activation sums of every group of this split, 32 values per thread,
-    // combined in a fixed order.
-    for (int idx = threadIdx.x; idx < M * gs * 4; idx += 256) {
-        const int m = idx / (gs * 4), rem = idx - m * gs * 4;
-        const int gl = rem >> 2, part = rem & 3;
-        const u4v* p = reinterpret_cast<const u4v*>(L.x + (size_t)m * L.K + (size_t)(g0 + gl) * kGroup + 32 * part);
-        float acc = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            u4v v = p[q];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                acc += (float)__builtin_bit_cast(_Float16, (uint16_t)(v[w] & 0xFFFFu));
-                acc += (float)__builtin_bit_cast(_Float16, (uint16_t)(v[w] >> 16));
-            }
-        }
-        acc += __shfl_xor(acc, 1);
-        acc += __shfl_xor(acc, 2);
-        if (part == 0) xsum[m * gs + gl] = acc;
-    }
-    __syncthreads();
-
-    const int wb = L.bounds[split * kWaves + wave], we = L.bounds[split * kWaves + wave + 1];
     float yacc[MB][4];
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) yacc[rb][r] = 0.f;
-
-    uint32_t DA[32], DB[32];
-    u4v XA[MB], XB[MB];
-    uint16_t sA = 0, sB = 0;
-    int bA = 2, bB = 2;
-    if (wb < we) load_group<MB>(L, wb, M, n, lane, DA, XA, sA, bA);
-    for (int g = wb; g < we; g += 2) {
-        if (g + 1 < we) load_group<MB>(L, g + 1, M, n, lane, DB, XB, sB, bB);
-        group_dispatch<MB>(bA, DA, XA, sA, xsum + (g - g0), gs, M, yacc);
-        if (g + 1 < we) {
-            if (g + 2 < we) load_group<MB>(L, g + 2, M, n, lane, DA, XA, sA, bA);
-            group_dispatch<MB>(bB, DB, XB, sB, xsum + (g + 1 - g0), gs, M, yacc);
-        }
+    {
+        const uint32_t* ord = L.order + gptr<uint16_t>(L.bounds)[wave];
+        const EXQ_GLOBAL uint16_t* cnt = gptr<uint16_t>(L.runs) + wave * kNumWidths;
+        int k;
+        if ((k = cnt[0]) > 0) { run_width<2, MB, TC, M1>(L, c, ord, k, yacc); ord += k; }
+        if ((k = cnt[1]) > 0) { run_width<3, MB, TC, M1>(L, c, ord, k, yacc); ord += k; }
+        if ((k = cnt[2]) > 0) { run_width<4, MB, TC, M1>(L, c, ord, k, yacc); ord += k; }
+        if ((k = cnt[3]) > 0) { run_width<5, MB, TC, M1>(L, c, ord, k, yacc); ord += k; }
+        if ((k = cnt[4]) > 0) { run_width<6, MB, TC, M1>(L, c, ord, k, yacc); ord += k; }
+        if ((k = cnt[5]) > 0) { run_width<8, MB, TC, M1>(L, c, ord, k, yacc); }
     }
 
+    // TC = 16: quarters ((q0 + q1) + (q2 + q3)) in every lane of a column.
+    // Then waves, in order, through LDS.
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * rb + r < M) red[(wave * M + 4 * rb + r) * 64 + lane] = yacc[rb][r];
-    __syncthreads();
-
-    const int ncol0 = tile * kTileCols;
-    if (L.S == 1) {
-        for (int t = threadIdx.x; t < M * 64; t += 256) {
-            const int m = t >> 6, c = t & 63;
-            float v = red[(0 * M + m) * 64 + c];
-            v += red[(1 * M + m) * 64 + c];
-            v += red[(2 * M + m) * 64 + c];
-            v += red[(3 * M + m) * 64 + c];
-            L.y[(size_t)m * L.N + ncol0 + c] = f32_to_f16_bits(v);
+        for (int r = 0; r < 4; ++r) {
+            float v = yacc[rb][r];
+            if constexpr (TC == 16) {
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+            }
+            if (4 * rb + r < M && lane < TC) red[(wave * M + 4 * rb + r) * TC + lane] = v;
         }
-        return;
-    }
-    for (int t = threadIdx.x; t < M * 64; t += 256) {
-        const int m = t >> 6, c = t & 63;
-        float v = red[(0 * M + m) * 64 + c];
-        v += red[(1 * M + m) * 64 + c];
-        v += red[(2 * M + m) * 64 + c];
-        v += red[(3 * M + m) * 64 + c];
-        L.partial[((size_t)split * M + m) * L.N + ncol0 + c] = v;
-    }
-    __threadfence();
     __syncthreads();
-    __shared__ int last;
-    if (threadIdx.x == 0) last = (atomicAdd(&L.counters[tile], 1u) == (uint32_t)(L.S - 1));
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    for (int t = threadIdx.x; t < M * 64; t += 256) {
-        const int m = t >> 6, c = t & 63;
-        float v = 0.f;
-        for (int sp = 0; sp < L.S; ++sp) v += L.partial[((size_t)sp * M + m) * L.N + ncol0 + c];
-        L.y[(size_t)m * L.N + ncol0 + c] = f32_to_f16_bits(v);
+    for (int t = threadIdx.x; t < M * TC; t += kWaves * 64) {
+        const int m = t / TC, col = t % TC;
+        float v = red[(0 * M + m) * TC + col];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) v += red[(w * M + m) * TC + col];
+        *gptr_w<uint16_t>(L.y + (size_t)m * L.N + tile * TC + col) = f32_to_f16_bits(v);
     }
-    if (threadIdx.x == 0) L.counters[tile] = 0u;
 }
 
-template <int MB>
-__global__ __launch_bounds__(256) void decode_kernel(LinearDev L, int M) {
-    extern __shared__ float lds[];
-    decode_wg<MB>(L, blockIdx.x, M, lds);
+template <int MB, int TC, bool M1>
+__global__ __launch_bounds__(kWaves * 64) void decode_kernel(LinearDev L, int M) {
+    __shared__ float red[kWaves * 4 * MB * TC];
+    decode_wg<MB, TC, M1>(L, blockIdx.x, M, red);
 }
 
-template <int MB>
-__global__ __launch_bounds__(256) void decode_plan_kernel(const LinearDev* __restrict__ list,
-                                                          const uint16_t* __restrict__ wg_map, int M) {
-    extern __shared__ float lds[];
-    const int li = wg_map[blockIdx.x];
-    const LinearDev L = list[li];
-    decode_wg<MB>(L, blockIdx.x - L.wg_begin, M, lds);
+template <int MB, bool M1>
+__global__ __launch_bounds__(kWaves * 64) void decode_plan_kernel(const LinearDev* __restrict__ list,
+                                                                   const uint32_t* __restrict__ wg_map, int M) {
+    __shared__ float red[kWaves * 4 * MB * 64];
+    const uint32_t e = gptr<uint32_t>(wg_map)[blockIdx.x];   // linear | tile << 16
+    LinearDev L;
+    {
+        static_assert(sizeof(LinearDev) % 4 == 0, "descriptor copy");
+        const EXQ_GLOBAL uint32_t* src = gptr<uint32_t>(list + (e & 0xFFFFu));
+        uint32_t* dst = reinterpret_cast<uint32_t*>(&L);
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(LinearDev) / 4); ++i) dst[i] = src[i];
+    }
+    decode_wg<MB, 64, M1>(L, (int)(e >> 16), M, red);
 }
 
 // ---------------------------------------------------------------- dequant
 
+// One lane per (column, quarter): decodes its 32 codes of group g and writes
+// fp16_RNE((c - z) * s) to w_out[k][n].
 template <int B>
-__device__ __forceinline__ void dequant_group(const uint32_t (&D)[32], float s, int N, int n, uint16_t* out) {
+__device__ __forceinline__ void dequant_quarter(const LinearDev& L, size_t P, int g, int n, int q,
+                                                uint16_t* __restrict__ w_out) {
+    uint32_t Q[B];
+    load_quarter<B>(L.qweight, (size_t)L.N, P, (size_t)n, q, Q);
+    const uint16_t s16 = *gptr<uint16_t>(L.scales + (size_t)g * L.N + n);
+    const float s = (float)__builtin_bit_cast(_Float16, s16);
     constexpr int C = Width<B>::per;
     constexpr int z = 1 << (B - 1);
-    static_for<0, 32>([&](auto UC) {
+    static_for<0, 8>([&](auto UC) {
         constexpr int U = decltype(UC)::value;
         constexpr int o = Width<B>::p0 * (U % C);
         uint32_t b0, b1;
-        unit_pair<B, U>(D, b0, b1);
-        const uint32_t c[4] = {(b0 & 0xFFFFu) >> o, b0 >> (16 + o), (b1 & 0xFFFFu) >> o, b1 >> (16 + o)};
+        unit_pair<B, U>(Q, b0, b1);
+        const uint32_t cv[4] = {(b0 & 0xFFFFu) >> o, b0 >> (16 + o), (b1 & 0xFFFFu) >> o, b1 >> (16 + o)};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // (c - z) * s is exact in fp32; one rounding to fp16.
-            const float w = (float)((int)c[e] - z) * s;
-            out[(size_t)(4 * U + e) * N + n] = f32_to_f16_bits(w);
+            const float w = (float)((int)cv[e] - z) * s;
+            const size_t k = (size_t)g * kGroup + 32 * q + 4 * U + e;
+            *gptr_w<uint16_t>(w_out + k * L.N + n) = f32_to_f16_bits(w);
         }
     });
 }
 
 __global__ __launch_bounds__(64) void dequant_kernel(LinearDev L, uint16_t* __restrict__ w_out) {
     const int g = blockIdx.y;
-    const int n = blockIdx.x * kTileCols + threadIdx.x;
-    uint32_t D[32];
-    u4v X[1];
-    uint16_t s16;
-    int b;
-    // reuse the decode loader; x is not needed but its row-0 load is harmless
-    load_group<1>(L, g, 1, n, threadIdx.x, D, X, s16, b);
-    const float s = (float)__builtin_bit_cast(_Float16, s16);
-    uint16_t* out = w_out + (size_t)g * kGroup * L.N;
-    switch (b) {
-        case 2: dequant_group<2>(D, s, L.N, n, out); break;
-        case 3: dequant_group<3>(D, s, L.N, n, out); break;
-        case 4: dequant_group<4>(D, s, L.N, n, out); break;
-        case 5: dequant_group<5>(D, s, L.N, n, out); break;
-        case 6: dequant_group<6>(D, s, L.N, n, out); break;
-        default: dequant_group<8>(D, s, L.N, n, out); break;
+    const int n = blockIdx.x * kTileCols + (threadIdx.x & 15);
+    const int q = threadIdx.x >> 4;
+    const uint32_t meta = gptr<uint32_t>(L.meta)[g];
+    const size_t P = meta >> 4;
+    switch (meta & 15u) {
+        case 2: dequant_quarter<2>(L, P, g, n, q, w_out); break;
+        case 3: dequant_quarter<3>(L, P, g, n, q, w_out); break;
+        case 4: dequant_quarter<4>(L, P, g, n, q, w_out); break;
+        case 5: dequant_quarter<5>(L, P, g, n, q, w_out); break;
+        case 6: dequant_quarter<6>(L, P, g, n, q, w_out); break;
+        default: dequant_quarter<8>(L, P, g, n, q, w_out); break;
     }
 }
 
@@ -351,19 +442,17 @@ struct exq_layer {
     std::vector<uint8_t> widths;
     const void* qweight;
     const void* scales;
-    SplitPlan plan;
+    WavePlan plan;
     uint32_t* d_meta = nullptr;
+    uint32_t* d_order = nullptr;
     uint16_t* d_bounds = nullptr;
-    float* d_partial = nullptr;
-    uint32_t* d_counters = nullptr;
-    uint16_t* d_zero_x = nullptr;  // K fp16 zeros, a valid x for the dequant launch
+    uint16_t* d_runs = nullptr;
 };
 
 struct exq_plan {
     int count = 0, M = 1, total_wgs = 0;
-    size_t lds_bytes = 0;
     LinearDev* d_list = nullptr;
-    uint16_t* d_wg_map = nullptr;
+    uint32_t* d_wg_map = nullptr;
 };
 
 namespace {
@@ -375,11 +464,6 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-int env_int(const char* name, int dflt) {
-    const char* v = getenv(name);
-    return v ? atoi(v) : dflt;
-}
-
 exq_status hip_fail(hipError_t e, const char* what) {
     return fail(EXQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -389,48 +473,78 @@ LinearDev linear_dev(const exq_layer* L, const void* x, void* y) {
     d.qweight = static_cast<const uint8_t*>(L->qweight);
     d.scales = static_cast<const uint16_t*>(L->scales);
     d.meta = L->d_meta;
+    d.order = L->d_order;
     d.bounds = L->d_bounds;
+    d.runs = L->d_runs;
     d.x = static_cast<const uint16_t*>(x);
     d.y = static_cast<uint16_t*>(y);
-    d.partial = L->d_partial;
-    d.counters = L->d_counters;
     d.K = L->K;
     d.N = L->N;
     d.G = L->G;
-    d.S = L->plan.S;
     d.tiles = L->N / kTileCols;
     d.wg_begin = 0;
     return d;
 }
 
-size_t decode_lds_bytes(int M, int split_groups) {
-    return sizeof(float) * (size_t)(((M * split_groups + 3) & ~3) + kWaves * M * 64);
+// Tile width for a single-linear launch: 64 columns when that still gives a
+// workgroup per CU, else 16.
+int tile_cols_for(int N) { return N / 64 >= 256 ? 64 : 16; }
+
+template <int MB, int TC, bool M1>
+void launch_decode_t(LinearDev d, int M, hipStream_t stream) {
+    d.tiles = d.N / TC;
+    hipLaunchKernelGGL((decode_kernel<MB, TC, M1>), dim3(d.tiles), dim3(kWaves * 64), 0, stream, d, M);
 }
 
-exq_status launch_decode(const LinearDev& d, int M, int max_split_groups, hipStream_t stream) {
-    const size_t lds = decode_lds_bytes(M, max_split_groups);
-    const dim3 grid(d.tiles * d.S), block(256);
+template <int TC>
+void launch_decode_mb(const LinearDev& d, int M, hipStream_t stream) {
     switch ((M + 3) / 4) {
-        case 1: hipLaunchKernelGGL(decode_kernel<1>, grid, block, lds, stream, d, M); break;
-        case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, lds, stream, d, M); break;
-        case 3: hipLaunchKernelGGL(decode_kernel<3>, grid, block, lds, stream, d, M); break;
-        default: hipLaunchKernelGGL(decode_kernel<4>, grid, block, lds, stream, d, M); break;
+        case 1:
+            if (M == 1) launch_decode_t<1, TC, true>(d, M, stream);
+            else launch_decode_t<1, TC, false>(d, M, stream);
+            break;
+        case 2: launch_decode_t<2, TC, false>(d, M, stream); break;
+        case 3: launch_decode_t<3, TC, false>(d, M, stream); break;
+        default: launch_decode_t<4, TC, false>(d, M, stream); break;
     }
+}
+
+exq_status launch_decode(const LinearDev& d, int M, hipStream_t stream) {
+    if (tile_cols_for(d.N) == 64) launch_decode_mb<64>(d, M, stream);
+    else launch_decode_mb<16>(d, M, stream);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? EXQ_OK : hip_fail(e, "decode launch");
+}
+
+template <int MB, bool M1>
+void launch_plan_t(const exq_plan* P, hipStream_t s) {
+    hipLaunchKernelGGL((decode_plan_kernel<MB, M1>), dim3(P->total_wgs), dim3(kWaves * 64), 0, s, P->d_list,
+                       P->d_wg_map, P->M);
+}
+
+void launch_plan(const exq_plan* P, hipStream_t s) {
+    switch ((P->M + 3) / 4) {
+        case 1:
+            if (P->M == 1) launch_plan_t<1, true>(P, s);
+            else launch_plan_t<1, false>(P, s);
+            break;
+        case 2: launch_plan_t<2, false>(P, s); break;
+        case 3: launch_plan_t<3, false>(P, s); break;
+        default: launch_plan_t<4, false>(P, s); break;
+    }
 }
 
 }  // namespace
 
 extern exq_status exq_prefill_launch(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream);
 
-// Decode kernel over consecutive 16-row slices of x (any M).
+// Decode kernel over consecutive slices of at most 16 rows of x (any M).
 exq_status exq_decode_rows(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream) {
     for (int r0 = 0; r0 < M; r0 += kMaxDecodeM) {
         const int m = std::min(kMaxDecodeM, M - r0);
         const void* xs = static_cast<const uint16_t*>(x) + (size_t)r0 * L->K;
         void* ys = static_cast<uint16_t*>(y) + (size_t)r0 * L->N;
-        exq_status st = launch_decode(linear_dev(L, xs, ys), m, L->plan.max_split_groups, stream);
+        exq_status st = launch_decode(linear_dev(L, xs, ys), m, stream);
         if (st != EXQ_OK) return st;
     }
     return EXQ_OK;
@@ -444,13 +558,17 @@ exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_
     *out = nullptr;
     exq_status st = check_layer_shape(K, N, group_size, widths_host);
     if (st != EXQ_OK) return st;
-    if (N % kTileCols) return fail(EXQ_ERR_INVALID_ARG, "N=%d is not a multiple of 64", N);
+    if (N % 64) return fail(EXQ_ERR_INVALID_ARG, "N=%d is not a multiple of 64", N);
     if (!d_qweight || !d_scales) return fail(EXQ_ERR_INVALID_ARG, "NULL device buffer");
     if (!aligned16(d_qweight) || !aligned16(d_scales))
         return fail(EXQ_ERR_INVALID_ARG, "qweight and scales must be 16-byte aligned");
     const int G = K / kGroup;
-    if ((size_t)8 * (size_t)G >= (1u << 28))
-        return fail(EXQ_ERR_UNSUPPORTED, "K too large for 28-bit per-column word offsets");
+    {
+        size_t words = 0;
+        for (int g = 0; g < G; ++g) words += widths_host[g];
+        if (words >= 65536 || G >= 65536)
+            return fail(EXQ_ERR_UNSUPPORTED, "K=%d is too large for 16-bit per-column word offsets", K);
+    }
     exq_layer* L = new (std::nothrow) exq_layer();
     if (!L) return fail(EXQ_ERR_OOM, "host allocation");
     L->K = K;
@@ -459,29 +577,22 @@ exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_
     L->widths.assign(widths_host, widths_host + G);
     L->qweight = d_qweight;
     L->scales = d_scales;
-    L->plan = plan_splits(K, N, widths_host, env_int("EXQ_FORCE_SPLITS", 0));
+    L->plan = plan_waves(K, widths_host);
     std::vector<uint32_t> meta = group_meta(K, widths_host);
-    const int tiles = N / kTileCols;
     hipError_t e = hipSuccess;
     auto cleanup = [&](exq_status s) { exq_layer_destroy(L); return s; };
-    if ((e = hipMalloc(&L->d_meta, sizeof(uint32_t) * G)) != hipSuccess) return cleanup(fail(EXQ_ERR_OOM, "hipMalloc meta"));
-    if ((e = hipMalloc(&L->d_bounds, sizeof(uint16_t) * L->plan.bounds.size())) != hipSuccess)
-        return cleanup(fail(EXQ_ERR_OOM, "hipMalloc bounds"));
-    if ((e = hipMalloc(&L->d_zero_x, sizeof(uint16_t) * K)) != hipSuccess) return cleanup(fail(EXQ_ERR_OOM, "hipMalloc x"));
-    if (L->plan.S > 1) {
-        if ((e = hipMalloc(&L->d_partial, sizeof(float) * (size_t)L->plan.S * kMaxDecodeM * N)) != hipSuccess)
-            return cleanup(fail(EXQ_ERR_OOM, "hipMalloc workspace"));
-        if ((e = hipMalloc(&L->d_counters, sizeof(uint32_t) * tiles)) != hipSuccess)
-            return cleanup(fail(EXQ_ERR_OOM, "hipMalloc counters"));
-        if ((e = hipMemset(L->d_counters, 0, sizeof(uint32_t) * tiles)) != hipSuccess)
-            return cleanup(hip_fail(e, "hipMemset counters"));
-    }
-    if ((e = hipMemcpy(L->d_meta, meta.data(), sizeof(uint32_t) * G, hipMemcpyHostToDevice)) != hipSuccess)
-        return cleanup(hip_fail(e, "hipMemcpy meta"));
-    if ((e = hipMemcpy(L->d_bounds, L->plan.bounds.data(), sizeof(uint16_t) * L->plan.bounds.size(),
+    if ((e = hipMalloc(&L->d_meta, sizeof(uint32_t) * G)) != hipSuccess ||
+        (e = hipMalloc(&L->d_order, sizeof(uint32_t) * G)) != hipSuccess ||
+        (e = hipMalloc(&L->d_bounds, sizeof(uint16_t) * L->plan.bounds.size())) != hipSuccess ||
+        (e = hipMalloc(&L->d_runs, sizeof(uint16_t) * L->plan.runs.size())) != hipSuccess)
+        return cleanup(fail(EXQ_ERR_OOM, "hipMalloc layer metadata"));
+    if ((e = hipMemcpy(L->d_meta, meta.data(), sizeof(uint32_t) * G, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(L->d_order, L->plan.order.data(), sizeof(uint32_t) * G, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(L->d_bounds, L->plan.bounds.data(), sizeof(uint16_t) * L->plan.bounds.size(),
+                       hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(L->d_runs, L->plan.runs.data(), sizeof(uint16_t) * L->plan.runs.size(),
                        hipMemcpyHostToDevice)) != hipSuccess)
-        return cleanup(hip_fail(e, "hipMemcpy bounds"));
-    if ((e = hipMemset(L->d_zero_x, 0, sizeof(uint16_t) * K)) != hipSuccess) return cleanup(hip_fail(e, "hipMemset x"));
+        return cleanup(hip_fail(e, "hipMemcpy layer metadata"));
     *out = L;
     return EXQ_OK;
 }
@@ -489,10 +600,9 @@ exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_
 void exq_layer_destroy(exq_layer_t L) {
     if (!L) return;
     if (L->d_meta) (void)hipFree(L->d_meta);
+    if (L->d_order) (void)hipFree(L->d_order);
     if (L->d_bounds) (void)hipFree(L->d_bounds);
-    if (L->d_partial) (void)hipFree(L->d_partial);
-    if (L->d_counters) (void)hipFree(L->d_counters);
-    if (L->d_zero_x) (void)hipFree(L->d_zero_x);
+    if (L->d_runs) (void)hipFree(L->d_runs);
     delete L;
 }
 
@@ -504,14 +614,14 @@ exq_status exq_gemm(const void* x, int M, exq_layer_t L, void* y, void* stream) 
     if (overlap(x, 2 * (size_t)M * L->K, y, 2 * (size_t)M * L->N)) return fail(EXQ_ERR_INVALID_ARG, "y overlaps x");
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (M > kMaxDecodeM) return exq_prefill_launch(L, x, M, y, s);
-    return launch_decode(linear_dev(L, x, y), M, L->plan.max_split_groups, s);
+    return exq_decode_rows(L, x, M, y, s);
 }
 
 exq_status exq_dequant(exq_layer_t L, void* w_out, void* stream) {
     if (!L) return fail(EXQ_ERR_INVALID_ARG, "layer is NULL");
     if (!w_out) return fail(EXQ_ERR_INVALID_ARG, "w_out is NULL");
     if (!aligned16(w_out)) return fail(EXQ_ERR_INVALID_ARG, "w_out must be 16-byte aligned");
-    LinearDev d = linear_dev(L, L->d_zero_x, nullptr);
+    LinearDev d = linear_dev(L, nullptr, nullptr);
     hipLaunchKernelGGL(dequant_kernel, dim3(L->N / kTileCols, L->G), dim3(64), 0, static_cast<hipStream_t>(stream), d,
                        static_cast<uint16_t*>(w_out));
     hipError_t e = hipGetLastError();
@@ -524,14 +634,13 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
     *out = nullptr;
     if (count < 1 || !layers || !xs || !ys) return fail(EXQ_ERR_INVALID_ARG, "empty or NULL plan arrays");
     if (M < 1 || M > kMaxDecodeM) return fail(EXQ_ERR_INVALID_ARG, "plan M=%d must be in [1, 16]", M);
+    if (count > 65535) return fail(EXQ_ERR_UNSUPPORTED, "plan of %d linears (at most 65535)", count);
+    for (int i = 0; i < count; ++i)
+        if (!layers[i] || !xs[i] || !ys[i]) return fail(EXQ_ERR_INVALID_ARG, "plan entry %d is NULL", i);
     std::vector<LinearDev> list(count);
-    std::vector<uint16_t> wg_map;
-    int max_groups = 0;
+    std::vector<int> work(count);
     for (int i = 0; i < count; ++i) {
         const exq_layer* L = layers[i];
-        if (!L || !xs[i] || !ys[i]) return fail(EXQ_ERR_INVALID_ARG, "plan entry %d is NULL", i);
-        for (int j = 0; j < i; ++j)
-            if (layers[j] == L) return fail(EXQ_ERR_INVALID_ARG, "layer of entry %d repeats entry %d (shared workspace)", i, j);
         if (!aligned16(xs[i]) || !aligned16(ys[i])) return fail(EXQ_ERR_INVALID_ARG, "plan entry %d misaligned", i);
         for (int j = 0; j < count; ++j) {
             if (overlap(ys[i], 2 * (size_t)M * L->N, xs[j], 2 * (size_t)M * layers[j]->K))
@@ -540,27 +649,35 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
                 return fail(EXQ_ERR_INVALID_ARG, "outputs %d and %d overlap", i, j);
         }
         list[i] = linear_dev(L, xs[i], const_cast<void*>(ys[i]));
-        list[i].wg_begin = (int)wg_map.size();
-        const int wgs = list[i].tiles * list[i].S;
-        if (i >= 65535 || wg_map.size() + wgs > (size_t)INT32_MAX)
-            return fail(EXQ_ERR_UNSUPPORTED, "plan too large");
-        wg_map.insert(wg_map.end(), wgs, (uint16_t)i);
-        max_groups = std::max(max_groups, L->plan.max_split_groups);
+        list[i].tiles = L->N / 64;
+        int words = 0;
+        for (int g = 0; g < L->G; ++g) words += L->widths[g];
+        work[i] = words + L->G;   // per-workgroup cost, as in the wave plan
     }
+    // Longest workgroups first, so the launch does not end on a tail of
+    // long-K tiles; within a linear, tiles in order.
+    std::vector<int> byw(count);
+    for (int i = 0; i < count; ++i) byw[i] = i;
+    std::stable_sort(byw.begin(), byw.end(), [&](int a, int b) { return work[a] > work[b]; });
+    std::vector<uint32_t> wg_map;
+    for (int i : byw)
+        for (int t = 0; t < list[i].tiles; ++t) wg_map.push_back((uint32_t)i | ((uint32_t)t << 16));
+    if (wg_map.size() > (size_t)INT32_MAX) return fail(EXQ_ERR_UNSUPPORTED, "plan too large");
+    for (int i = 0; i < count; ++i)
+        if (list[i].tiles >= 65536) return fail(EXQ_ERR_UNSUPPORTED, "entry %d has too many tiles", i);
     exq_plan* P = new (std::nothrow) exq_plan();
     if (!P) return fail(EXQ_ERR_OOM, "host allocation");
     P->count = count;
     P->M = M;
     P->total_wgs = (int)wg_map.size();
-    P->lds_bytes = decode_lds_bytes(M, max_groups);
     hipError_t e;
     if ((e = hipMalloc(&P->d_list, sizeof(LinearDev) * count)) != hipSuccess ||
-        (e = hipMalloc(&P->d_wg_map, sizeof(uint16_t) * wg_map.size())) != hipSuccess) {
+        (e = hipMalloc(&P->d_wg_map, sizeof(uint32_t) * wg_map.size())) != hipSuccess) {
         exq_plan_destroy(P);
         return fail(EXQ_ERR_OOM, "hipMalloc plan");
     }
     if ((e = hipMemcpy(P->d_list, list.data(), sizeof(LinearDev) * count, hipMemcpyHostToDevice)) != hipSuccess ||
-        (e = hipMemcpy(P->d_wg_map, wg_map.data(), sizeof(uint16_t) * wg_map.size(), hipMemcpyHostToDevice)) !=
+        (e = hipMemcpy(P->d_wg_map, wg_map.data(), sizeof(uint32_t) * wg_map.size(), hipMemcpyHostToDevice)) !=
             hipSuccess) {
         exq_plan_destroy(P);
         return hip_fail(e, "hipMemcpy plan");
@@ -571,14 +688,7 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
 
 exq_status exq_plan_run(exq_plan_t P, void* stream) {
     if (!P) return fail(EXQ_ERR_INVALID_ARG, "plan is NULL");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 grid(P->total_wgs), block(256);
-    switch ((P->M + 3) / 4) {
-        case 1: hipLaunchKernelGGL(decode_plan_kernel<1>, grid, block, P->lds_bytes, s, P->d_list, P->d_wg_map, P->M); break;
-        case 2: hipLaunchKernelGGL(decode_plan_kernel<2>, grid, block, P->lds_bytes, s, P->d_list, P->d_wg_map, P->M); break;
-        case 3: hipLaunchKernelGGL(decode_plan_kernel<3>, grid, block, P->lds_bytes, s, P->d_list, P->d_wg_map, P->M); break;
-        default: hipLaunchKernelGGL(decode_plan_kernel<4>, grid, block, P->lds_bytes, s, P->d_list, P->d_wg_map, P->M); break;
-    }
+    launch_plan(P, static_cast<hipStream_t>(stream));
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? EXQ_OK : hip_fail(e, "plan launch");
 }

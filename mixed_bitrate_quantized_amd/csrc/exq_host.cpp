@@ -108,44 +108,38 @@ std::vector<uint32_t> group_meta(int K, const uint8_t* widths) {
     return meta;
 }
 
-// --------------------------------------------------------------- splitting
+// ------------------------------------------------------------ wave plan
 
-SplitPlan plan_splits(int K, int N, const uint8_t* widths, int forced_splits) {
+WavePlan plan_waves(int K, const uint8_t* widths) {
     const int G = K / kGroup;
-    const int tiles = N / kTileCols;
-    SplitPlan p;
-    int S;
-    if (forced_splits > 0) {
-        S = forced_splits;
-    } else {
-        // Aim for >= 512 workgroups per layer (two per CU on 256 CUs) while
-        // keeping at least two groups per wave.
-        S = (512 + tiles - 1) / tiles;
-        S = std::min(S, std::max(1, G / (2 * kWaves)));
-    }
-    S = std::max(1, std::min(S, std::max(1, G / kWaves)));
-    // Groups in one split must fit the per-workgroup x-sum table.
-    while ((G + S - 1) / S > kMaxSplitGroups) ++S;
-    p.S = S;
-    // Byte-balanced cut points: cost of a group ~ b_g words per column plus a
-    // fixed share for its scale, activation load and epilogue.
+    WavePlan p;
+    std::vector<uint32_t> prefix(G + 1, 0);
+    for (int g = 0; g < G; ++g) prefix[g + 1] = prefix[g] + widths[g];
+    std::vector<int> idx(G);
+    for (int g = 0; g < G; ++g) idx[g] = g;
+    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return widths[a] < widths[b]; });
+    p.order.resize(G);
+    for (int i = 0; i < G; ++i) p.order[i] = (uint32_t)idx[i] | (prefix[idx[i]] << 16);
+    // Byte-balanced cuts of the sorted list: a group costs b_g words per
+    // column plus a fixed share for its scale, activations and epilogue.
     std::vector<double> cum(G + 1, 0.0);
-    for (int g = 0; g < G; ++g) cum[g + 1] = cum[g] + widths[g] + 0.75;
-    const int parts = S * kWaves;
-    p.bounds.assign(parts + 1, 0);
-    p.bounds[parts] = (uint16_t)G;
-    int g = 0;
-    for (int i = 1; i < parts; ++i) {
-        double target = cum[G] * i / parts;
-        while (g < G && cum[g + 1] <= target) ++g;
-        // choose the nearer of g and g+1
-        int cut = g;
-        if (g < G && (cum[g + 1] - target) < (target - cum[g])) cut = g + 1;
-        cut = std::max<int>(cut, p.bounds[i - 1]);
-        p.bounds[i] = (uint16_t)cut;
+    for (int i = 0; i < G; ++i) cum[i + 1] = cum[i] + widths[idx[i]] + 1.0;
+    p.bounds.assign(kWaves + 1, 0);
+    p.bounds[kWaves] = (uint16_t)G;
+    int i = 0;
+    for (int w = 1; w < kWaves; ++w) {
+        double target = cum[G] * w / kWaves;
+        while (i < G && cum[i + 1] <= target) ++i;
+        int cut = i;
+        if (i < G && (cum[i + 1] - target) < (target - cum[i])) cut = i + 1;
+        cut = std::max<int>(cut, p.bounds[w - 1]);
+        p.bounds[w] = (uint16_t)cut;
     }
-    for (int s = 0; s < S; ++s)
-        p.max_split_groups = std::max(p.max_split_groups, (int)p.bounds[(s + 1) * kWaves] - (int)p.bounds[s * kWaves]);
+    p.runs.assign((size_t)kWaves * kNumWidths, 0);
+    for (int w = 0; w < kWaves; ++w)
+        for (int j = p.bounds[w]; j < p.bounds[w + 1]; ++j)
+            for (int wi = 0; wi < kNumWidths; ++wi)
+                if (widths[idx[j]] == kWidthOrder[wi]) p.runs[(size_t)w * kNumWidths + wi]++;
     return p;
 }
 

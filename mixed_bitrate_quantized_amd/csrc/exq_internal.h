@@ -10,10 +10,9 @@
 namespace exq {
 
 constexpr int kGroup = 128;     // input channels per group
-constexpr int kTileCols = 64;   // output columns per workgroup tile (one per lane)
-constexpr int kWaves = 4;       // waves per decode workgroup, each takes a slice of K
+constexpr int kTileCols = 16;   // output columns per decode workgroup (lane % 16)
+constexpr int kWaves = 8;       // waves per decode workgroup, each takes a share of the groups
 constexpr int kMaxDecodeM = 16; // largest M served by the decode kernel
-constexpr int kMaxSplitGroups = 1024;
 
 // Records a message for exq_last_error() and returns `s`.
 exq_status fail(exq_status s, const char* fmt, ...);
@@ -23,16 +22,23 @@ bool width_supported(int b);
 // Validation shared by every entry point that describes a layer.
 exq_status check_layer_shape(int K, int N, int group_size, const uint8_t* widths);
 
-// Split of a layer's K range: S workgroups per column tile, each of which
-// gives its kWaves waves contiguous, byte-balanced runs of groups.
-// bounds has S*kWaves + 1 entries; run (s, w) = [bounds[s*kWaves+w], bounds[s*kWaves+w+1]).
-struct SplitPlan {
-    int S = 1;
+// How the kWaves waves of a decode workgroup share a layer's groups.  All
+// groups are sorted by (width, index) and cut into kWaves contiguous,
+// byte-balanced chunks, so each wave streams one or two runs of equal-width
+// groups with a fixed number of loads per group.
+//   order[i] = g | (P_g << 16) in that sorted order;
+//   bounds[w] .. bounds[w+1] is wave w's chunk of `order`;
+//   runs[w*6 + i] counts its groups of width kWidthOrder[i].
+constexpr int kNumWidths = 6;
+constexpr int kWidthOrder[kNumWidths] = {2, 3, 4, 5, 6, 8};
+
+struct WavePlan {
+    std::vector<uint32_t> order;
     std::vector<uint16_t> bounds;
-    int max_split_groups = 0;   // largest number of groups in one split
+    std::vector<uint16_t> runs;
 };
 
-SplitPlan plan_splits(int K, int N, const uint8_t* widths, int forced_splits);
+WavePlan plan_waves(int K, const uint8_t* widths);
 
 // Per-group metadata word read by the kernels: (P_g << 4) | b_g.
 std::vector<uint32_t> group_meta(int K, const uint8_t* widths);

@@ -154,14 +154,18 @@ int oracle_pack(const uint8_t* codes, int K, int N, const uint8_t* widths, uint8
     if (K % ORACLE_GROUP) return 1;
     int G = K / ORACLE_GROUP;
     memset(qweight, 0, (size_t)oracle_packed_bytes(K, N, widths));
-    uint64_t Pg = 0;
+    for (int g = 0; g < G; ++g)
+        if (!width_ok(widths[g])) return 1;
+    int bad = 0;
+    /* groups own disjoint byte ranges, so they can be filled concurrently */
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int g = 0; g < G; ++g) {
         int b = widths[g];
-        if (!width_ok(b)) return 1;
+        uint64_t Pg = prefix_words(widths, g);
         for (int n = 0; n < N; ++n) {
             for (int k = 0; k < ORACLE_GROUP; ++k) {
                 int c = codes[(size_t)n * K + (size_t)g * ORACLE_GROUP + k];
-                if (c < 0 || c >= (1 << b)) return 1;
+                if (c >= (1 << b)) { bad = 1; continue; }
                 int shift = 0;
                 for (int plane = 0; plane < 2; ++plane) {
                     int dw, bit;
@@ -173,22 +177,22 @@ int oracle_pack(const uint8_t* codes, int K, int N, const uint8_t* widths, uint8
                 }
             }
         }
-        Pg += (uint64_t)b;
     }
-    return 0;
+    return bad;
 }
 
 int oracle_unpack(const uint8_t* qweight, int K, int N, const uint8_t* widths, uint8_t* codes) {
     if (K % ORACLE_GROUP) return 1;
     int G = K / ORACLE_GROUP;
-    uint64_t Pg = 0;
+    for (int g = 0; g < G; ++g)
+        if (!width_ok(widths[g])) return 1;
+#pragma omp parallel for schedule(dynamic, 1)
     for (int g = 0; g < G; ++g) {
         int b = widths[g];
-        if (!width_ok(b)) return 1;
+        uint64_t Pg = prefix_words(widths, g);
         for (int n = 0; n < N; ++n)
             for (int k = 0; k < ORACLE_GROUP; ++k)
                 codes[(size_t)n * K + (size_t)g * ORACLE_GROUP + k] = (uint8_t)read_code(qweight, N, Pg, b, n, k);
-        Pg += (uint64_t)b;
     }
     return 0;
 }
@@ -207,6 +211,8 @@ int oracle_quantize(const float* W, int K, int N, const uint8_t* widths, uint8_t
         int b = widths[g];
         if (!width_ok(b)) return 1;
         int z = 1 << (b - 1), qmax = z - 1;
+        int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
         for (int n = 0; n < N; ++n) {
             const float* w = W + (size_t)n * K + (size_t)g * ORACLE_GROUP;
             float amax = 0.0f;
@@ -216,7 +222,7 @@ int oracle_quantize(const float* W, int K, int N, const uint8_t* widths, uint8_t
             }
             volatile float quotient = amax / (float)qmax;
             uint16_t s16 = oracle_f16_from_double((double)quotient);
-            if ((s16 & 0x7C00u) == 0x7C00u) return 2;
+            if ((s16 & 0x7C00u) == 0x7C00u) { overflow = 1; continue; }
             scales[(size_t)g * N + n] = s16;
             float s = (float)oracle_f16_to_double(s16);
             uint8_t* c = codes + (size_t)n * K + (size_t)g * ORACLE_GROUP;
@@ -229,6 +235,7 @@ int oracle_quantize(const float* W, int K, int N, const uint8_t* widths, uint8_t
                 c[i] = (uint8_t)((int)q + z);
             }
         }
+        if (overflow) return 2;
     }
     return 0;
 }
@@ -238,6 +245,7 @@ int oracle_quantize(const float* W, int K, int N, const uint8_t* widths, uint8_t
 /* w_hat fp16 bits [K][N] row-major from codes [N][K] and scales [G][N]. */
 int oracle_dequant(const uint8_t* codes, const uint16_t* scales, int K, int N, const uint8_t* widths, uint16_t* w_hat) {
     if (K % ORACLE_GROUP) return 1;
+#pragma omp parallel for schedule(static)
     for (int k = 0; k < K; ++k) {
         int g = k / ORACLE_GROUP, b = widths[g], z = 1 << (b - 1);
         for (int n = 0; n < N; ++n) {

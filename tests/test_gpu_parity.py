@@ -69,12 +69,15 @@ def test_single_group_each_width(exq, b):
     full_check(exq, W, [b], [1, 6], "single-b%d" % b)
 
 
-@pytest.mark.parametrize("splits", [1, 2, 5])
-def test_forced_split_counts(exq, splits, monkeypatch):
-    monkeypatch.setenv("EXQ_FORCE_SPLITS", str(splits))
-    widths = [2, 2, 3, 8, 2, 4, 2, 6, 5, 2, 3, 2, 2, 3, 2, 2, 2, 2, 3, 2]
-    W = synth.weight(synth.seed_for("splits"), 320, 128 * len(widths))
-    full_check(exq, W, widths, [1, 4, 16], "splits%d" % splits)
+@pytest.mark.parametrize("widths", [
+    [2, 2, 3, 8, 2, 4, 2, 6, 5, 2, 3, 2, 2, 3, 2, 2, 2, 2, 3, 2],   # 20 groups, every width
+    [8, 3, 2],                                                    # fewer groups than waves
+    [2] * 40 + [3] * 9 + [6, 8, 4, 5],                            # long runs, one wave per width
+    [5, 6, 8, 8, 6, 5, 4, 3, 2, 8, 8, 8, 8],                      # wide groups dominate
+])
+def test_wave_chunking(exq, widths):
+    W = synth.weight(synth.seed_for("chunks", *widths), 320, 128 * len(widths))
+    full_check(exq, W, widths, [1, 4, 16], "chunks%d" % len(widths))
 
 
 def test_zero_and_one_hot_and_doubling(exq):
@@ -163,23 +166,26 @@ def test_determinism_and_guard_bands(exq):
     layer.close()
 
 
-def test_plan_matches_individual_calls(exq):
+def test_plan_matches_oracle_and_is_repeatable(exq):
     specs = [(256, 64, [2, 3]), (512, 192, [8, 2, 6, 5]), (1024, 128, [2] * 7 + [4]), (384, 320, [3, 3, 4])]
-    layers, xs, ys, singles = [], [], [], []
+    layers, refs = [], []
     for i, (K, N, widths) in enumerate(specs):
         W = synth.weight(synth.seed_for("plan", i), N, K)
-        layer, *_ = make_layer(exq, W, widths)
+        layer, codes, s_ref, _ = make_layer(exq, W, widths)
         layers.append(layer)
+        refs.append(oracle.dequant(codes, s_ref, widths))
     for M in (1, 3, 16):
-        xs = [to_dev(synth.activations(synth.seed_for("plan-x", i, M), M, l.K)) for i, l in enumerate(layers)]
+        xs_h = [synth.activations(synth.seed_for("plan-x", i, M), M, l.K) for i, l in enumerate(layers)]
+        xs = [to_dev(x) for x in xs_h]
         ys = [torch.empty((M, l.N), dtype=torch.float16, device="cuda") for l in layers]
         note("plan M=%d" % M)
         plan = exq.Plan(layers, xs, ys, M)
         plan.run()
-        got = [y_to_np(y) for y in ys]
-        for l, x, g in zip(layers, xs, got):
-            np.testing.assert_array_equal(g, y_to_np(l.gemm(x)))
-        plan.run()   # split-K counters are left at zero: a second run is identical
+        got = [y_to_np(y).copy() for y in ys]
+        for x, g, w_ref, l in zip(xs_h, got, refs, layers):
+            y_ref, bnd = oracle.gemm(x, w_ref)
+            assert_within(g, y_ref, bnd, "plan M=%d N=%d" % (M, l.N))
+        plan.run()
         for y, g in zip(ys, got):
             np.testing.assert_array_equal(y_to_np(y), g)
         plan.close()

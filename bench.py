@@ -1,0 +1,279 @@
+"""Benchmark: mixed-bitrate quantized decode over a Llama-3-70B-shaped weight stack on one MI355X.
+
+A step is one decode pass (M = 1 token by default) through all 80 decoder
+blocks' seven linears (q, k, v, o, gate, up, down = 560 linears, ~22.9 GB of
+2.55-bpw EXQ1 weights), each block's seven independent linears issued as one
+exq plan launch.  Inputs are seeded synthetic tensors of the model's shapes
+(no trained weights); they are resident in HBM before timing starts.
+
+Prints one JSON line: whole-step HBM throughput (algorithmic bytes / step
+time), ms/step, the decode kernel's roofline and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 5|3] [--m 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_plan_70b_m1_counters.json")
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("exq_device.hip", "exq_internal.h"):
+        with open(os.path.join(ROOT, "mixed_bitrate_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def build_stack(exq, torch, specs, M, keep_first=0):
+    """Generate, pack (host) and upload every linear; returns layers, xs, ys, bytes, kept W."""
+    from synth import workloads
+    layers, xs, ys, kept = [], [], [], []
+    total = 0
+    t0 = time.time()
+    wbuf = None
+    for i, spec in enumerate(specs):
+        if wbuf is None or wbuf.size < spec.N * spec.K:
+            wbuf = np.empty(spec.N * spec.K, dtype=np.float32)
+        W = wbuf[: spec.N * spec.K].reshape(spec.N, spec.K)
+        workloads.make_weight(spec, out=W)
+        widths = workloads.make_widths(spec, W)
+        q, s = exq.exq_pack(W, widths)
+        if i < keep_first:
+            kept.append((spec, W.copy(), widths))
+        layers.append(exq.Layer(spec.K, spec.N, widths, q, s))
+        xs.append(torch.from_numpy(workloads.make_x(spec, M)).cuda())
+        ys.append(torch.empty((M, spec.N), dtype=torch.float16, device="cuda"))
+        total += workloads.algorithmic_bytes(spec.K, spec.N, widths, M)
+        if (i + 1) % 70 == 0 or i + 1 == len(specs):
+            log("packed %d/%d linears (%.1f GB algorithmic) in %.0fs" % (i + 1, len(specs), total / 1e9, time.time() - t0))
+    return layers, xs, ys, total, kept
+
+
+def omp_threads() -> int:
+    import ctypes
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+        return int(gomp.omp_get_max_threads())
+    except OSError:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(kept, M, gpu_ys):
+    """Time the CPU oracle (as it stands) on the kept linears: its own quantize+pack
+    (untimed), then the timed path from packed storage -- bit-by-bit unpack,
+    dequantize, fp64 matmul -- over every output column."""
+    import oracle
+    from synth import workloads
+    secs, nbytes, worst = 0.0, 0, 0.0
+    for (spec, W, widths), y_gpu in zip(kept, gpu_ys):
+        _, s_ref, q_ref = oracle.reference_layer(W, widths)
+        x = workloads.make_x(spec, M)
+        cols = np.arange(spec.N, dtype=np.int64)
+        t0 = time.perf_counter()
+        y_ref, bnd = oracle.gemm_packed_cols(x, q_ref, s_ref, widths, spec.K, spec.N, cols)
+        secs += time.perf_counter() - t0
+        nbytes += workloads.algorithmic_bytes(spec.K, spec.N, widths, M)
+        _, w = oracle.within_tolerance(y_gpu.astype(np.float64), y_ref, bnd)
+        worst = max(worst, w)
+    return secs, nbytes, worst
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=5, choices=(3, 5))
+    ap.add_argument("--m", type=int, default=1)
+    ap.add_argument("--blocks", type=int, default=None, help="limit the number of 70B blocks (config 5)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=1, help="blocks of the workload the oracle is timed on")
+    ap.add_argument("--variants", action="store_true", help="also time per-linear calls, ungraphed and graphed")
+    ap.add_argument("--calib-copy-gib", type=float, default=0.0,
+                    help="run a plain device copy of this size (for counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import mixed_bitrate_quantized_amd as exq
+    from synth import workloads, BLOCK_SHAPES
+
+    if args.calib_copy_gib > 0:
+        n = int(args.calib_copy_gib * (1 << 30)) // 2
+        a = torch.empty(n, dtype=torch.float16, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copied %d bytes three times" % (2 * n))
+        return
+
+    M = args.m
+    specs = workloads.linears(args.config)
+    if args.blocks is not None:
+        specs = specs[: args.blocks * len(BLOCK_SHAPES)]
+    nblk = len(specs) // len(BLOCK_SHAPES)
+    keep = 0 if args.no_cpu_baseline else args.cpu_blocks * len(BLOCK_SHAPES)
+    layers, xs, ys, step_bytes, kept = build_stack(exq, torch, specs, M, keep_first=keep)
+    plans = []
+    for b in range(nblk):
+        sl = slice(b * len(BLOCK_SHAPES), (b + 1) * len(BLOCK_SHAPES))
+        plans.append(exq.Plan(layers[sl], xs[sl], ys[sl], M))
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step():
+        for p in plans:
+            p.run(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # Timed region: exactly `steps` steps between two events on the launch stream.
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_begin.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_begin.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    # The decode kernel's own duration: an event pair around every plan
+    # launch, over a second pass of the same steps (events between launches
+    # would otherwise add their own gaps to the step time above).
+    starts = [[torch.cuda.Event(enable_timing=True) for _ in plans] for _ in range(args.steps)]
+    ends = [[torch.cuda.Event(enable_timing=True) for _ in plans] for _ in range(args.steps)]
+    for s in range(args.steps):
+        for b, p in enumerate(plans):
+            starts[s][b].record(stream)
+            p.run(stream)
+            ends[s][b].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = np.array([[starts[s][b].elapsed_time(ends[s][b]) for b in range(nblk)] for s in range(args.steps)])
+    kernel_ms = float(launch_ms.mean())
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    bytes_per_launch = step_bytes / nblk
+    achieved = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
+    log("step %.3f ms, %.1f GB/s; decode launch %.1f us (%.1f GB/s)" % (ms_step, gbs, kernel_ms * 1e3, achieved))
+
+    traffic = None
+    if os.path.exists(PROFILE_COUNTERS):
+        with open(PROFILE_COUNTERS) as f:
+            prof = json.load(f)
+        if prof.get("kernel_source_hash") == kernel_source_hash() and prof.get("config") == args.config and prof.get("m") == M:
+            traffic = prof.get("hbm_bytes_per_launch")
+
+    extra = {}
+    if args.variants:
+        def timed(fn, reps):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        reps = max(3, args.steps // 5)
+        whole = exq.Plan(layers, xs, ys, M)
+        extra["ms_per_step_one_launch"] = timed(lambda: whole.run(stream), reps)
+        whole.close()
+
+        def calls():
+            s = torch.cuda.current_stream()
+            for l, x, y in zip(layers, xs, ys):
+                exq.exq_gemm(x.data_ptr(), M, l.handle, y.data_ptr(), s)
+        extra["ms_per_step_separate_calls"] = timed(calls, reps)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls()
+        torch.cuda.synchronize()
+        extra["ms_per_step_separate_calls_graphed"] = timed(g.replay, reps)
+        del g
+        step()
+        torch.cuda.synchronize()
+
+    cpu = None
+    if kept:
+        log("timing the CPU oracle on %d linears" % len(kept))
+        gpu_ys = [ys[i].cpu().numpy() for i in range(len(kept))]
+        secs, cbytes, worst = cpu_baseline(kept, M, gpu_ys)
+        cpu = {
+            "value": round(cbytes / secs / 1e9, 4),
+            "unit": "GB/s",
+            "cores": omp_threads(),
+            "kind": "oracle",
+            "sample": "%d linears (block%s 0..%d of the same stack) at M=%d, every output column: bit-by-bit "
+                      "unpack + dequant + fp64 matmul from the oracle's own packed layer; %.1f s for %.2f GB; "
+                      "worst GPU error / tolerance on the sample %.3f" % (len(kept), "s" if args.cpu_blocks > 1 else "",
+                                                                         args.cpu_blocks - 1, M, secs, cbytes / 1e9, worst),
+        }
+
+    out = {
+        "metric": "quant GEMV eff. HBM GB/s (% peak) + ms/step, 70B-shaped 2.55bpw M=" + str(M),
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 in, fp32 accumulate, EXQ1 2-8 bit codes",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) fp16 activations)",
+        "config": {
+            "workload": ("llama3-70b-shaped decoder stack: %d blocks x 7 linears, mixed 2.55 bpw, M=%d" % (nblk, M))
+            if args.config == 5 else "one llama3-70b-shaped block (7 linears), mixed 2.55 bpw, M=%d" % M,
+            "linears": len(specs),
+            "bytes_per_step": step_bytes,
+            "launches_per_step": nblk,
+            "parallelism": "1 GPU",
+        },
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_plan_kernel (one launch = one block's 7 linears)",
+            "bytes_per_launch": bytes_per_launch,
+            "avg_launch_us": round(kernel_ms * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+    out.update(extra)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -49,7 +49,19 @@ struct LinearDev {
     const uint16_t* x;        // fp16 [M][K]
     uint16_t* y;              // fp16 [M][N]
     int K, N, G, tiles, wg_begin;
+    uint32_t qbytes;          // bytes of qweight (< 2^31)
+    uint32_t sbytes;          // bytes of scales
 };
+
+// Weights and scales are read with raw buffer loads.  A load whose offset is
+// past the buffer's size returns zeros without touching memory: the
+// pipeline's tail steps use that to keep a fixed load count per step at no
+// memory cost.
+constexpr uint32_t kBufOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
 
 // Global-address-space views: loads through them are global_load (vmcnt
 // only), never flat_load, whose lgkmcnt coupling would make every LDS read
@@ -121,20 +133,22 @@ template <int B> __device__ constexpr float class_factor(int t) {
     return (float)(1u << (24 - Width<B>::p0 * t));
 }
 
-// Loads the B dwords of quarter q of column n, group at word offset P.
-// Plane p occupies column-local dwords [m0 + q*p, m0 + (q+1)*p): a p-dword
-// piece of one 16-byte word for p <= 4, two whole words for p = 8.
+// Loads the B dwords of quarter q of the column whose word 0 (of this group)
+// is at byte `col` of the weight buffer (kBufOOB: a tail step, zeros).  Plane
+// p occupies column-local dwords [m0 + q*p, m0 + (q+1)*p): a p-dword piece of
+// one 16-byte word for p <= 4, two whole words for p = 8.  nt: streamed once.
 template <int P_DW>
-__device__ __forceinline__ void load_piece(const uint8_t* col, size_t N, int m, uint32_t* dst) {
-    const uint8_t* a = col + 16 * (size_t)(m >> 2) * N + 4 * (m & 3);
+__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t rw, uint32_t col, uint32_t N16, int m,
+                                           uint32_t* dst) {
+    const uint32_t off = col + (uint32_t)(m >> 2) * N16 + 4u * (uint32_t)(m & 3);
     if constexpr (P_DW == 1) {
-        dst[0] = __builtin_nontemporal_load(gptr<uint32_t>(a));
+        dst[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 2);
     } else if constexpr (P_DW == 2) {
-        const u2v v = __builtin_nontemporal_load(gptr<u2v>(a));
+        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, 2);
         dst[0] = v[0];
         dst[1] = v[1];
     } else {
-        const u4v v = __builtin_nontemporal_load(gptr<u4v>(a));
+        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 2);
         dst[0] = v[0];
         dst[1] = v[1];
         dst[2] = v[2];
@@ -143,27 +157,25 @@ __device__ __forceinline__ void load_piece(const uint8_t* col, size_t N, int m, 
 }
 
 template <int B>
-__device__ __forceinline__ void load_quarter(const uint8_t* qw, size_t N, size_t P, size_t n, int q,
+__device__ __forceinline__ void load_quarter(__amdgpu_buffer_rsrc_t rw, uint32_t col, uint32_t N16, int q,
                                              uint32_t (&Q)[B]) {
     using T = Width<B>;
-    const uint8_t* col = qw + 16 * (N * P + n);
     if constexpr (T::p0 == 8) {
-        load_piece<4>(col, N, 8 * q, Q);
-        load_piece<4>(col, N, 8 * q + 4, Q + 4);
+        load_piece<4>(rw, col, N16, 8 * q, Q);
+        load_piece<4>(rw, col, N16, 8 * q + 4, Q + 4);
     } else {
-        load_piece<T::p0>(col, N, T::p0 * q, Q);
+        load_piece<T::p0>(rw, col, N16, T::p0 * q, Q);
     }
-    if constexpr (T::p1 > 0) load_piece<T::p1>(col, N, 4 * T::p0 + T::p1 * q, Q + T::p0);
+    if constexpr (T::p1 > 0) load_piece<T::p1>(rw, col, N16, 4 * T::p0 + T::p1 * q, Q + T::p0);
 }
 
-// All B words of column n of the group at word offset P (one 1 KB wave load each).
+// All B words of one column of a group (one 1 KB wave load each).
 template <int B>
-__device__ __forceinline__ void load_group_words(const uint8_t* qw, size_t N, size_t P, size_t n,
+__device__ __forceinline__ void load_group_words(__amdgpu_buffer_rsrc_t rw, uint32_t col, uint32_t N16,
                                                  uint32_t (&D)[4 * B]) {
-    const EXQ_GLOBAL u4v* base = gptr<u4v>(qw) + (N * P + n);
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-        const u4v v = __builtin_nontemporal_load(base + (size_t)j * N);
+        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, col + (uint32_t)j * N16, 0, 2);
         D[4 * j + 0] = v[0];
         D[4 * j + 1] = v[1];
         D[4 * j + 2] = v[2];
@@ -173,6 +185,7 @@ __device__ __forceinline__ void load_group_words(const uint8_t* qw, size_t N, si
 
 struct DecodeCtx {
     int M, lane, q, n;
+    __amdgpu_buffer_rsrc_t rw, rs;   // weight and scale buffers
 };
 
 template <int TC> struct Tile {
@@ -267,35 +280,41 @@ __device__ __forceinline__ void group_compute(const DecodeCtx& c, const uint32_t
 }
 
 template <int B, int TC> struct Depth {
-    // groups in flight per wave (the current one included)
+    // groups in flight per wave (the one being computed included)
     static constexpr int value = TC == 64 ? ((B <= 2) ? 4 : (B <= 4 ? 3 : 2)) : ((B <= 3) ? 6 : (B <= 6 ? 4 : 3));
 };
 
 // A run of `cnt` width-B groups (entries ord[0..cnt)), pipelined DEPTH deep:
 // while group i is computed, groups i+1 .. i+DEPTH-1 are in flight.  Every
 // step issues exactly one group's loads -- weights, scale, activation
-// operands, in that order -- with the index clamped at the end of the run,
-// so each wait is a compile-time count.
+// operands, in that order -- so each wait is a compile-time count.  Steps
+// past the end of the run load from an out-of-range buffer offset: they
+// keep the count fixed, return zeros and cost no memory traffic.
 template <int B, int MB, int TC, bool M1>
 __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c, const uint32_t* ord, int cnt,
                                           float (&yacc)[MB][4]) {
     constexpr int DEPTH = Depth<B, TC>::value;
     constexpr int NDW = B * Tile<TC>::NQ;
     uint32_t Q[DEPTH][NDW];
-    u4v X[DEPTH][MB];
     uint16_t S[DEPTH];
+    u4v X[DEPTH][MB];
     const EXQ_GLOBAL uint32_t* og = gptr<uint32_t>(ord);
-    auto issue = [&](uint32_t e, uint32_t (&Qd)[NDW], u4v (&Xd)[MB], uint16_t& Sd) {
-        const int g = (int)(e & 0xFFFFu);
-        if constexpr (TC == 64) load_group_words<B>(L.qweight, (size_t)L.N, (size_t)(e >> 16), (size_t)c.n, Qd);
-        else load_quarter<B>(L.qweight, (size_t)L.N, (size_t)(e >> 16), (size_t)c.n, c.q, Qd);
-        Sd = *gptr<uint16_t>(L.scales + (size_t)g * L.N + c.n);
+    const uint32_t N16 = 16u * (uint32_t)L.N;
+    auto issue = [&](int step, uint32_t (&Qd)[NDW], uint16_t& Sd, u4v (&Xd)[MB]) {
+        const bool valid = step < cnt;
+        const uint32_t e = og[min(step, cnt - 1)];
+        const uint32_t g = e & 0xFFFFu, P = e >> 16;
+        const uint32_t col = valid ? 16u * ((uint32_t)L.N * P + (uint32_t)c.n) : kBufOOB;
+        if constexpr (TC == 64) load_group_words<B>(c.rw, col, N16, Qd);
+        else load_quarter<B>(c.rw, col, N16, c.q, Qd);
+        const uint32_t soff = valid ? 2u * (g * (uint32_t)L.N + (uint32_t)c.n) : kBufOOB;
+        Sd = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(c.rs, soff, 0, 0);
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb) Xd[rb] = load_act<TC>(L, c, g, rb);
+        for (int rb = 0; rb < MB; ++rb) Xd[rb] = load_act<TC>(L, c, (int)g, rb);
     };
     static_for<0, DEPTH - 1>([&](auto KC) {
         constexpr int k = decltype(KC)::value;
-        issue(og[min(k, cnt - 1)], Q[k], X[k], S[k]);
+        issue(k, Q[k], S[k], X[k]);
     });
     for (int i = 0; i < cnt; i += DEPTH) {
         bool done = false;
@@ -306,7 +325,7 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
                 done = true;
                 return;
             }
-            issue(og[min(i + k + DEPTH - 1, cnt - 1)], Q[nk], X[nk], S[nk]);
+            issue(i + k + DEPTH - 1, Q[nk], S[nk], X[nk]);
             group_compute<B, MB, TC, M1>(c, Q[k], X[k], S[k], yacc);
         });
     }
@@ -323,6 +342,8 @@ __device__ __forceinline__ void decode_wg(const LinearDev& L, int tile, int M, f
     c.lane = lane;
     c.q = TC == 64 ? 0 : lane >> 4;
     c.n = tile * TC + (TC == 64 ? lane : (lane & 15));
+    c.rw = buffer_rsrc(L.qweight, L.qbytes);
+    c.rs = buffer_rsrc(L.scales, L.sbytes);
 
     float yacc[MB][4];
 #pragma unroll
@@ -394,7 +415,8 @@ template <int B>
 __device__ __forceinline__ void dequant_quarter(const LinearDev& L, size_t P, int g, int n, int q,
                                                 uint16_t* __restrict__ w_out) {
     uint32_t Q[B];
-    load_quarter<B>(L.qweight, (size_t)L.N, P, (size_t)n, q, Q);
+    load_quarter<B>(buffer_rsrc(L.qweight, L.qbytes), 16u * ((uint32_t)L.N * (uint32_t)P + (uint32_t)n),
+                    16u * (uint32_t)L.N, q, Q);
     const uint16_t s16 = *gptr<uint16_t>(L.scales + (size_t)g * L.N + n);
     const float s = (float)__builtin_bit_cast(_Float16, s16);
     constexpr int C = Width<B>::per;
@@ -483,6 +505,10 @@ LinearDev linear_dev(const exq_layer* L, const void* x, void* y) {
     d.G = L->G;
     d.tiles = L->N / kTileCols;
     d.wg_begin = 0;
+    size_t words = 0;
+    for (int g = 0; g < L->G; ++g) words += L->widths[g];
+    d.qbytes = (uint32_t)(16 * words * (size_t)L->N);
+    d.sbytes = (uint32_t)(2 * (size_t)L->G * (size_t)L->N);
     return d;
 }
 
@@ -568,6 +594,9 @@ exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_
         for (int g = 0; g < G; ++g) words += widths_host[g];
         if (words >= 65536 || G >= 65536)
             return fail(EXQ_ERR_UNSUPPORTED, "K=%d is too large for 16-bit per-column word offsets", K);
+        if (16 * words * (size_t)N >= kBufOOB)
+            return fail(EXQ_ERR_UNSUPPORTED, "packed layer of %zu bytes exceeds the 2 GiB per-layer limit",
+                        16 * words * (size_t)N);
     }
     exq_layer* L = new (std::nothrow) exq_layer();
     if (!L) return fail(EXQ_ERR_OOM, "host allocation");

@@ -1,5 +1,5 @@
 // Device half of libexq for gfx950: decode GEMV, dequantization, layer and
-// plan management.  The prefill GEMM lives in exq_prefill.hip.
+// plan management.  The prefill GEMM (M > 16) lives in exq_prefill.hip.
 //
 // Decode design (M <= 16, HBM-bound):
 //   * a workgroup owns 16 output columns over the whole of K; its 8 waves
@@ -29,131 +29,14 @@
 #include <type_traits>
 #include <vector>
 
+#include "exq_device_common.h"
 #include "exq_internal.h"
 
 namespace exq {
 
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-typedef uint32_t u2v __attribute__((ext_vector_type(2)));
-
-// Everything a kernel needs about one linear of a launch.
-struct LinearDev {
-    const uint8_t* qweight;   // EXQ1 words
-    const uint16_t* scales;   // fp16 [G][N]
-    const uint32_t* meta;     // [G]: (P_g << 4) | b_g
-    const uint32_t* order;    // [G]: g | (P_g << 16), sorted by width
-    const uint16_t* bounds;   // [kWaves + 1] wave chunks of `order`
-    const uint16_t* runs;     // [kWaves][6] groups of width 2,3,4,5,6,8 per chunk
-    const uint16_t* x;        // fp16 [M][K]
-    uint16_t* y;              // fp16 [M][N]
-    int K, N, G, tiles, wg_begin;
-    uint32_t qbytes;          // bytes of qweight (< 2^31)
-    uint32_t sbytes;          // bytes of scales
-};
-
-// Weights and scales are read with raw buffer loads.  A load whose offset is
-// past the buffer's size returns zeros without touching memory: the
-// pipeline's tail steps use that to keep a fixed load count per step at no
-// memory cost.
-constexpr uint32_t kBufOOB = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-
-// Global-address-space views: loads through them are global_load (vmcnt
-// only), never flat_load, whose lgkmcnt coupling would make every LDS read
-// wait for all weight loads in flight.
-#define EXQ_GLOBAL __attribute__((address_space(1)))
-template <class T> __device__ __forceinline__ const EXQ_GLOBAL T* gptr(const void* p) {
-    return (const EXQ_GLOBAL T*)p;
-}
-template <class T> __device__ __forceinline__ EXQ_GLOBAL T* gptr_w(void* p) { return (EXQ_GLOBAL T*)p; }
-
-template <int I> using IC = std::integral_constant<int, I>;
-
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(IC<B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
-// Plane split of a width: plane 0 of p0 bits, plane 1 of p1 bits (or none).
-template <int B> struct Width {
-    static constexpr int p0 = (B <= 3) ? 2 : (B == 8 ? 8 : 4);
-    static constexpr int p1 = B - p0;
-    static constexpr int per = 8 / p0;            // decoder units per plane-0 dword
-    static constexpr int R = p1 ? p0 / p1 : 1;    // plane-0 dwords per plane-1 dword
-};
-
-__device__ __forceinline__ h4 as_h4(uint32_t a, uint32_t b) {
-    u2v v = {a, b};
-    return __builtin_bit_cast(h4, v);
-}
-
-__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
-    return __builtin_bit_cast(uint16_t, (_Float16)v);
-}
-
-// Decoder unit U of a width-B group, on the dwords of NQ consecutive
-// K-quarters (NQ = 4: the whole group, U in [0, 32); NQ = 1: quarter q, U in
-// [0, 8) covering codes 32q + 4U ..).  Q holds the NQ*p0 plane-0 dwords then
-// the NQ*p1 plane-1 dwords.  Returns two dwords whose 16-bit
-// halves hold codes 4U, 4U+1 (b0) and 4U+2, 4U+3 (b1), each at bit offset
-// o = p0 * (U % per) of its half, every other bit clear.  Read as fp16 the
-// halves are exactly c * 2^(o-24).  Bit positions follow the EXQ1 layout
-// (include/exq.h); the quarter split keeps dword-local positions unchanged.
-template <int B, int U, int NQ = 1>
-__device__ __forceinline__ void unit_pair(const uint32_t* Q, uint32_t& b0, uint32_t& b1) {
-    using T = Width<B>;
-    constexpr int d = U / T::per, t = U % T::per, o = T::p0 * t;
-    constexpr uint32_t mlo = (((1u << T::p0) - 1u) * 0x00010001u) << o;
-    const uint32_t lo0 = Q[d], lo1 = Q[d] >> 8;
-    if constexpr (T::p1 == 0) {
-        b0 = lo0 & mlo;
-        b1 = lo1 & mlo;
-    } else {
-        constexpr int h = d / T::R, delta = d % T::R;
-        constexpr uint32_t mhi = (((1u << T::p1) - 1u) * 0x00010001u) << (o + T::p0);
-        constexpr int sh0 = T::p0 - T::p1 * delta;      // left shift, high fields of codes 4U, 4U+1
-        constexpr int sh1 = T::p1 * delta + 8 - T::p0;  // right shift, codes 4U+2, 4U+3
-        static_assert(sh0 > 0 && sh1 > 0, "plane-1 alignment");
-        const uint32_t H = Q[NQ * T::p0 + h];
-        b0 = (lo0 & mlo) | ((H << sh0) & mhi);
-        b1 = (lo1 & mlo) | ((H >> sh1) & mhi);
-    }
-}
-
 template <int B> __device__ constexpr float class_factor(int t) {
     // 2^(24 - o), o = p0 * t: turns c * 2^(o-24) back into c.
     return (float)(1u << (24 - Width<B>::p0 * t));
-}
-
-// Loads the B dwords of quarter q of the column whose word 0 (of this group)
-// is at byte `col` of the weight buffer (kBufOOB: a tail step, zeros).  Plane
-// p occupies column-local dwords [m0 + q*p, m0 + (q+1)*p): a p-dword piece of
-// one 16-byte word for p <= 4, two whole words for p = 8.  nt: streamed once.
-template <int P_DW>
-__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t rw, uint32_t col, uint32_t N16, int m,
-                                           uint32_t* dst) {
-    const uint32_t off = col + (uint32_t)(m >> 2) * N16 + 4u * (uint32_t)(m & 3);
-    if constexpr (P_DW == 1) {
-        dst[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 2);
-    } else if constexpr (P_DW == 2) {
-        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, 2);
-        dst[0] = v[0];
-        dst[1] = v[1];
-    } else {
-        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 2);
-        dst[0] = v[0];
-        dst[1] = v[1];
-        dst[2] = v[2];
-        dst[3] = v[3];
-    }
 }
 
 template <int B>
@@ -210,12 +93,6 @@ __device__ __forceinline__ u4v load_act(const LinearDev& L, const DecodeCtx& c, 
 // operand lane are summed with dot2 against ones, then the lanes holding the
 // same row are combined by xor-shuffles in a fixed order.  Every lane ends
 // with the sum for row (its lane % 4); the row-r value is then broadcast.
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-
-// fp16 pair view of a dword.  The argument is a plain scalar on purpose:
-// __builtin_bit_cast applied directly to an ext_vector element (x[i]) has
-// been seen to read element 0 whatever i is.
-__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
 template <int TC>
 __device__ __forceinline__ float act_sum_lane(const u4v X) {
@@ -459,17 +336,6 @@ __global__ __launch_bounds__(64) void dequant_kernel(LinearDev L, uint16_t* __re
 
 using namespace exq;
 
-struct exq_layer {
-    int K, N, G;
-    std::vector<uint8_t> widths;
-    const void* qweight;
-    const void* scales;
-    WavePlan plan;
-    uint32_t* d_meta = nullptr;
-    uint32_t* d_order = nullptr;
-    uint16_t* d_bounds = nullptr;
-    uint16_t* d_runs = nullptr;
-};
 
 struct exq_plan {
     int count = 0, M = 1, total_wgs = 0;
@@ -490,7 +356,9 @@ exq_status hip_fail(hipError_t e, const char* what) {
     return fail(EXQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-LinearDev linear_dev(const exq_layer* L, const void* x, void* y) {
+}  // namespace
+
+LinearDev exq::linear_dev(const exq_layer* L, const void* x, void* y) {
     LinearDev d;
     d.qweight = static_cast<const uint8_t*>(L->qweight);
     d.scales = static_cast<const uint16_t*>(L->scales);
@@ -504,13 +372,14 @@ LinearDev linear_dev(const exq_layer* L, const void* x, void* y) {
     d.N = L->N;
     d.G = L->G;
     d.tiles = L->N / kTileCols;
-    d.wg_begin = 0;
     size_t words = 0;
     for (int g = 0; g < L->G; ++g) words += L->widths[g];
     d.qbytes = (uint32_t)(16 * words * (size_t)L->N);
     d.sbytes = (uint32_t)(2 * (size_t)L->G * (size_t)L->N);
     return d;
 }
+
+namespace {
 
 // Tile width for a single-linear launch: 64 columns when that still gives a
 // workgroup per CU, else 16.

@@ -44,3 +44,16 @@ WavePlan plan_waves(int K, const uint8_t* widths);
 std::vector<uint32_t> group_meta(int K, const uint8_t* widths);
 
 }  // namespace exq
+
+// A packed layer resident in device memory (the exq_layer_t handle).
+struct exq_layer {
+    int K, N, G;
+    std::vector<uint8_t> widths;
+    const void* qweight;      // borrowed
+    const void* scales;       // borrowed
+    exq::WavePlan plan;
+    uint32_t* d_meta = nullptr;
+    uint32_t* d_order = nullptr;
+    uint16_t* d_bounds = nullptr;
+    uint16_t* d_runs = nullptr;
+};

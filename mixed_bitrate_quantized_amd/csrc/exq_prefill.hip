@@ -2,25 +2,25 @@
 //
 // The pages place the dequantization inside the matmul kernel (the Q-GEMM
 // of the exllamav2 repository report, section "solution philosophy"); at
-// large M the product is compute-bound, so here the dequantized tile is
-// built once per workgroup in LDS and consumed by fp16 MFMA:
+// large M the product is compute-bound, so the codes are expanded once per
+// workgroup tile straight into MFMA operands:
 //   * a workgroup of 4 waves owns a 256 (rows of x) x 256 (output columns)
-//     tile of y over all of K; each wave computes a 128 x 128 quarter of it
-//     with v_mfma_f32_32x32x16_f16 into 16 fp32 accumulator blocks;
-//   * K advances in stages of 64 (half a group), double-buffered in LDS: an
-//     x tile [256 rows][64] and a W_hat tile [256 columns][64], both fp16
-//     and k-contiguous, rows padded to 72 halves so that the 16-byte operand
-//     reads of 8 or 16 consecutive rows fall in distinct banks;
-//   * thread t stages column t of the W_hat tile: it loads the packed words
-//     of its half group through fixed load slots (a slot the width does not
-//     use reads an out-of-range offset: zeros, no memory traffic) and
-//     dequantizes them exactly -- a code placed in the mantissa of an fp16
-//     whose exponent makes its value 2^(10-o) + c, one packed subtract gives
-//     c - z exactly and one packed multiply by the scale gives
+//     tile of y over all of K; wave w owns columns [64 w, 64 w + 64) of it and
+//     all 256 rows, 16 blocks of v_mfma_f32_32x32x16_f16 accumulators;
+//   * K advances in stages of 64 (half a group).  Within a stage the order of
+//     k is free as long as x follows it: MFMA k-slot 8 j + i of K-step kk is
+//     code 32 j + 8 kk + i of the half group, so lane l (j = l / 32) consumes
+//     exactly EXQ1 quarter 2 h + j of its column -- the 4 b bytes the decode
+//     kernel reads -- and decodes it itself, into its own A operands, with
+//     wave-uniform shifts and register picks.  W_hat never goes through LDS
+//     and no dequantized value is computed twice;
+//   * x is staged in LDS, [256 rows][64 k] per stage, double-buffered, rows
+//     padded to 72 halves so that 16-byte operand reads of 8 or 16
+//     consecutive rows fall in distinct banks; one barrier per stage;
+//   * decoding is exact and width-generic: a code goes into the low byte of
+//     an fp16 whose high byte is 0x64, which reads 1024 + c; one packed
+//     subtract of 1024 + z and one packed multiply by the scale give
 //     fp16_RNE((c - z) * s), the bits of the dequantization definition;
-//   * while the matrix cores work on stage s, the workgroup dequantizes
-//     stage s+1 (loaded during stage s-1) into the other buffer and issues
-//     the loads of stage s+2; one barrier per stage;
 //   * workgroup ids are mapped to tiles XCD-aware: the ids one XCD receives
 //     form a contiguous run of tiles in row-major order, so the x rows of a
 //     tile are shared through that XCD's L2.
@@ -36,28 +36,21 @@ namespace {
 
 constexpr int kPT = 256;        // tile rows of x and tile columns of W
 constexpr int kPK = 64;         // K per stage: half a group
-constexpr int kPLd = kPK + 8;   // padded LDS row length, halves
+constexpr int kPLd = kPK + 8;   // padded LDS row length of the x tile, halves
 constexpr int kPThreads = 256;  // 4 waves
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 
-// Packed weights of one stage for this thread's column.
-struct WRegs {
-    uint32_t q[16];   // plane-0 dwords of the half group: up to 4 words
-    uint32_t h[4];    // plane-1 dwords: up to 2 pieces of 2 dwords
-    uint32_t s;       // fp16 scale in the low half
-};
-
 struct PrefillCtx {
     __amdgpu_buffer_rsrc_t rw, rs, rx;
-    int tid, lane, wn0, wm0;
-    uint32_t n;       // the column this thread stages
-    bool n_ok;
+    int tid, lane, wave;
+    uint32_t q;        // K-quarter of the half group this lane decodes (lane / 32)
+    uint32_t col[2];   // its two columns (clamped into [0, N): extra columns are never stored)
 };
 
 // Where stage st comes from: half h = st % 2 of group g = st / 2.  A stage
-// past the last one reloads the last (L2 hits, never used): a uniform test
+// past the last one reloads the last (cache hits, never used): a uniform test
 // on it would split the stage into branches.
 struct StageSrc {
     uint32_t g, P, h;
@@ -75,35 +68,45 @@ __device__ __forceinline__ StageSrc stage_src(const LinearDev& L, int st, int S)
     return r;
 }
 
-// Packed words and scale of a stage.  Slots a width does not use read an
-// out-of-range offset: zeros, no memory traffic, fixed load count.
-__device__ __forceinline__ void issue_w(const LinearDev& L, const PrefillCtx& c, const StageSrc& src, WRegs& W) {
+// Packed words of one K-quarter of one column, and its scale.
+struct QRegs {
+    uint32_t q[8];   // plane-0 dwords (p0 of them)
+    uint32_t h[2];   // plane-1 dwords (p1 of them)
+    uint32_t s;      // fp16 scale in the low half
+};
+
+// Loads quarter 2h + j of the lane's two columns through fixed slots; a slot
+// the width does not use reads an out-of-range offset (zeros, no traffic).
+// Column-local dword m of group g sits at byte 16 (N P_g + (m / 4) N + n) + 4 (m % 4).
+__device__ __forceinline__ void issue_w(const LinearDev& L, const PrefillCtx& c, const StageSrc& src,
+                                        QRegs (&W)[2]) {
     const int b = src.b;
-    const int p0 = b <= 3 ? 2 : (b == 8 ? 8 : 4), p1 = b - p0, nw0 = p0 >> 1;
-    const uint32_t N16 = 16u * (uint32_t)L.N, h = src.h;
-    const bool ok = c.n_ok;
-    const uint32_t base = 16u * ((uint32_t)L.N * src.P + c.n);
+    const uint32_t p0 = b <= 3 ? 2u : (b == 8 ? 8u : 4u), p1 = (uint32_t)b - p0;
+    const uint32_t N16 = 16u * (uint32_t)L.N, qq = 2u * src.h + c.q;
+    const uint32_t m0 = p0 * qq, m1 = 4u * p0 + p1 * qq;
+    const uint32_t offA = (m0 >> 2) * N16 + 4u * (m0 & 3u);
+    const uint32_t offC = (m1 >> 2) * N16 + 4u * (m1 & 3u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (ok && i < nw0) ? base + ((uint32_t)nw0 * h + (uint32_t)i) * N16 : kBufOOB;
-        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(c.rw, off, 0, 0);
-        W.q[4 * i + 0] = v[0];
-        W.q[4 * i + 1] = v[1];
-        W.q[4 * i + 2] = v[2];
-        W.q[4 * i + 3] = v[3];
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t base = 16u * ((uint32_t)L.N * src.P + c.col[i]);
+        const u2v a0 = __builtin_amdgcn_raw_buffer_load_b64(c.rw, base + offA, 0, 0);
+        const u2v a1 = __builtin_amdgcn_raw_buffer_load_b64(c.rw, p0 >= 4 ? base + offA + 8u : kBufOOB, 0, 0);
+        const u4v bq = __builtin_amdgcn_raw_buffer_load_b128(c.rw, p0 == 8 ? base + offA + N16 : kBufOOB, 0, 0);
+        const uint32_t h0 = __builtin_amdgcn_raw_buffer_load_b32(c.rw, p1 >= 1 ? base + offC : kBufOOB, 0, 0);
+        const uint32_t h1 = __builtin_amdgcn_raw_buffer_load_b32(c.rw, p1 == 2 ? base + offC + 4u : kBufOOB, 0, 0);
+        W[i].q[0] = a0[0];
+        W[i].q[1] = a0[1];
+        W[i].q[2] = a1[0];
+        W[i].q[3] = a1[1];
+        W[i].q[4] = bq[0];
+        W[i].q[5] = bq[1];
+        W[i].q[6] = bq[2];
+        W[i].q[7] = bq[3];
+        W[i].h[0] = h0;
+        W[i].h[1] = h1;
+        W[i].s = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+            c.rs, 2u * (src.g * (uint32_t)L.N + c.col[i]), 0, 0);
     }
-    // plane 1: p1 = 1 -> dwords 2h, 2h+1 of word p0; p1 = 2 -> word p0 + h
-    const uint32_t w1 = base + ((uint32_t)p0 + (p1 == 2 ? h : 0u)) * N16 + (p1 == 1 ? 8u * h : 0u);
-    const uint32_t off0 = (ok && p1 > 0) ? w1 : kBufOOB;
-    const uint32_t off1 = (ok && p1 == 2) ? w1 + 8u : kBufOOB;
-    const u2v v0 = __builtin_amdgcn_raw_buffer_load_b64(c.rw, off0, 0, 0);
-    const u2v v1 = __builtin_amdgcn_raw_buffer_load_b64(c.rw, off1, 0, 0);
-    W.h[0] = v0[0];
-    W.h[1] = v0[1];
-    W.h[2] = v1[0];
-    W.h[3] = v1[1];
-    const uint32_t soff = ok ? 2u * (src.g * (uint32_t)L.N + c.n) : kBufOOB;
-    W.s = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(c.rs, soff, 0, 0);
 }
 
 // x chunk `it` of a stage: row it * 32 + tid / 8 of the tile, k chunk tid % 8.
@@ -114,12 +117,15 @@ __device__ __forceinline__ u4v issue_x(const LinearDev& L, const PrefillCtx& c, 
     return __builtin_amdgcn_raw_buffer_load_b128(c.rx, off, 0, 0);
 }
 
-// Width-generic decoding.  For unit U (codes 4U .. 4U+3 of the half group)
-// the plane-0 field of code 4U + e sits at bit o + 8 e2 + 16 e1 of dword
-// U p0 / 8 of the half's plane-0 dwords (o = (U p0) mod 8, e = e1 + 2 e2),
-// and its plane-1 field at bit o + p1 ((U p0 / 8) mod R) + 8 e2 + 16 e1 of
-// plane-1 dword U / 8 (p1 = 1) or U / 4 (p1 = 2) -- the EXQ1 layout restated
-// per half group.  Shifting the plane-0 dword right by o and rotating the
+__device__ __forceinline__ void store_x_chunk(const u4v& v, uint16_t* sx, int tid, int it) {
+    *reinterpret_cast<u4v*>(sx + (it * 32 + (tid >> 3)) * kPLd + 8 * (tid & 7)) = v;
+}
+
+// Width-generic decoding.  For unit U (codes 4U .. 4U+3 of a K-quarter) the
+// plane-0 field of code 4U + e sits at bit o + 8 e2 + 16 e1 of dword U p0 / 8
+// of the quarter's plane-0 dwords (o = (U p0) mod 8, e = e1 + 2 e2), and its
+// plane-1 field at bit o + p1 ((U p0 / 8) mod R) + 8 e2 + 16 e1 of plane-1
+// dword U p1 / 8 -- the EXQ1 layout restated per quarter.  Shifting the plane-0 dword right by o and rotating the
 // plane-1 dword right to bit p0, then merging under the plane-0 mask, leaves
 // code 4U + e in bits [0, b) of byte e2 + 2 e1 ("canonical" dword).  Every
 // width-dependent amount is a wave-uniform operand taken from this table.
@@ -129,9 +135,9 @@ struct DqRow {
     uint32_t mask0;     // bits [0, p0) of every byte
     uint32_t maskb;     // bits [0, b) of every byte
     uint32_t negc;      // fp16 pair -(1024 + z)
-    uint32_t sel4;      // all ones when p0 == 4: plane-0 dword U / 2
+    uint32_t sel4;      // all ones when p0 == 4: plane-0 dword U / 2 (else U / 4)
     uint32_t sel8;      // all ones when p0 == 8: plane-0 dword U
-    uint32_t sel6;      // all ones when p1 == 2: plane-1 dword U / 4
+    uint32_t sel6;      // all ones when p1 == 2: plane-1 dword U / 4 (else 0)
     uint32_t pad[2];
 };
 
@@ -171,24 +177,23 @@ __constant__ DqRow kDq[9] = {dq_row(0), dq_row(1), dq_row(2), dq_row(3), dq_row(
 
 __device__ __forceinline__ uint32_t pick(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
 
-// Part KK (units 4KK .. 4KK+3, k in [16KK, 16KK+16)) of the dequantization
-// of this thread's column of a half group into its LDS row: each code goes
-// into the low byte of an fp16 with high byte 0x64, whose value is then
-// 1024 + c; subtracting 1024 + z is exact and the multiply by the scale
-// rounds once, giving fp16_RNE((c - z) * s).
+// A operand of K-step kk for one column: units 2 kk and 2 kk + 1 of the
+// lane's quarter, i.e. codes 8 kk .. 8 kk + 7 as fp16_RNE((c - z) * s).  Each
+// code goes into the low byte of an fp16 with high byte 0x64 (value 1024 + c);
+// subtracting 1024 + z is exact and the multiply by the scale rounds once.
 template <int KK>
-__device__ __forceinline__ void dequant_part(const WRegs& W, const DqRow& T, uint16_t* wrow) {
+__device__ __forceinline__ h8 dequant_operand(const QRegs& W, const DqRow& T) {
     const h2 s2 = as_h2(W.s | (W.s << 16));
     const h2 nc = as_h2(T.negc);
-    uint32_t out[8];
-    static_for<0, 4>([&](auto VC) {
+    uint32_t out[4];
+    static_for<0, 2>([&](auto VC) {
         constexpr int V = decltype(VC)::value;
-        constexpr int U = 4 * KK + V;
+        constexpr int U = 2 * KK + V;
         uint32_t q = W.q[U >> 2];
         if constexpr ((U >> 1) != (U >> 2)) q = pick(T.sel4, W.q[U >> 1], q);
         if constexpr (U != (U >> 2)) q = pick(T.sel8, W.q[U], q);
-        uint32_t hv = W.h[U >> 3];
-        if constexpr ((U >> 2) != (U >> 3)) hv = pick(T.sel6, W.h[U >> 2], hv);
+        uint32_t hv = W.h[0];
+        if constexpr ((U >> 2) != 0) hv = pick(T.sel6, W.h[U >> 2], hv);
         const uint32_t lo = q >> T.shr[U & 3];
         const uint32_t hi = __builtin_amdgcn_alignbit(hv, hv, T.rot[U & 7]);
         const uint32_t canon = pick(T.mask0, lo, hi) & T.maskb;
@@ -197,43 +202,34 @@ __device__ __forceinline__ void dequant_part(const WRegs& W, const DqRow& T, uin
         out[2 * V] = __builtin_bit_cast(uint32_t, (as_h2(b0) + nc) * s2);
         out[2 * V + 1] = __builtin_bit_cast(uint32_t, (as_h2(b1) + nc) * s2);
     });
-    *reinterpret_cast<u4v*>(wrow + 16 * KK) = u4v{out[0], out[1], out[2], out[3]};
-    *reinterpret_cast<u4v*>(wrow + 16 * KK + 8) = u4v{out[4], out[5], out[6], out[7]};
+    const u4v v = {out[0], out[1], out[2], out[3]};
+    return __builtin_bit_cast(h8, v);
 }
 
-__device__ __forceinline__ void store_x_chunk(const u4v& v, uint16_t* sx, int tid, int it) {
-    *reinterpret_cast<u4v*>(sx + (it * 32 + (tid >> 3)) * kPLd + 8 * (tid & 7)) = v;
-}
-
-// MFMA operands of K-step kk (16 k) for this wave's 128 x 128 quarter.
-// Operand A is W_hat (rows = output columns n), operand B is x (columns =
-// rows m of x); lane l holds row l % 32 of a 32-block, k 8 (l / 32) .. +8.
-struct Frags {
-    h8 a[4], b[4];
+// Operands of one K-step: the wave's two W blocks (A) and eight x blocks (B).
+struct Ops {
+    h8 a[2], x[8];
 };
 
-__device__ __forceinline__ void load_frags(const uint16_t* sw, const uint16_t* sx, const PrefillCtx& c, int kk,
-                                           Frags& f) {
-    const int r = c.lane & 31, kh = (c.lane >> 5) * 8;
+// x operand of K-step kk: lane l holds row 32 jb + l % 32 of the tile and the
+// x values that meet its k-slots, k = 32 (l / 32) + 8 kk + [0, 8).
+__device__ __forceinline__ void load_x_ops(const uint16_t* sx, const PrefillCtx& c, int kk, Ops& o) {
+    const int off = (c.lane & 31) * kPLd + 32 * (c.lane >> 5) + 8 * kk;
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-        f.a[ib] = *reinterpret_cast<const h8*>(sw + (c.wn0 + 32 * ib + r) * kPLd + 16 * kk + kh);
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-        f.b[jb] = *reinterpret_cast<const h8*>(sx + (c.wm0 + 32 * jb + r) * kPLd + 16 * kk + kh);
+    for (int jb = 0; jb < 8; ++jb) o.x[jb] = *reinterpret_cast<const h8*>(sx + jb * 32 * kPLd + off);
 }
 
-__device__ __forceinline__ void mfma_frags(const Frags& f, f16v (&acc)[4][4]) {
+__device__ __forceinline__ void mfma_ops(const Ops& o, f16v (&acc)[2][8]) {
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+    for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-            acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[ib], f.b[jb], acc[ib][jb], 0, 0, 0);
+        for (int ib = 0; ib < 2; ++ib)
+            acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[ib], o.x[jb], acc[ib][jb], 0, 0, 0);
 }
 
 // Issue pattern of one region: each of its 16 MFMAs followed by up to four
-// VALU operations, one LDS operation and one global load, so that the
-// dequantization and staging run in the shadow of the matrix cores.
+// VALU operations, one LDS operation and one global load, so that decoding
+// and staging run in the shadow of the matrix cores.
 __device__ __forceinline__ void region_schedule() {
     static_for<0, 16>([&](auto) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
@@ -243,50 +239,47 @@ __device__ __forceinline__ void region_schedule() {
     });
 }
 
-// Stage st: multiply LDS buffer (rd_w, rd_x); stage st+1 (weights in Wn, x
-// chunks in xr, width row T) into buffer (wr_w, wr_x); load stage st+2 (src)
-// into Wf and, chunk by chunk as they are freed, into xr.
+// Stage st.  On entry LDS buffer rd_x holds stage st's x tile, Wc its packed
+// words, xr stage st+1's x chunks, `carry` the operands of the previous
+// stage's last K-step.  Region r reads and decodes the operands of K-step r
+// and multiplies K-step r - 1 (region 0: `carry`, prepared before the
+// barrier), so no MFMA waits for work issued in its own region; it also
+// moves two x chunks of stage st+1 into wr_x and loads those of stage st+2.
+// Stage st+1's packed words go into Wn.  sched_barrier keeps the regions
+// apart so the scheduler interleaves within a region without hoisting a
+// whole stage's operands.
 //
-// Four regions, one per K-step, separated by sched_barrier so the scheduler
-// interleaves a region's dequantization with its MFMAs without hoisting a
-// whole stage's operands.  Region r reads the operands of K-step r and
-// multiplies K-step r - 1; region 0 multiplies the previous stage's last
-// K-step (`carry`, read before the barrier), so no MFMA waits for an operand
-// read issued in its own region.  On return `carry` holds K-step 3.
-//
-// The scalars of the next stage (src_n: stage st+3, T_n: the width row of
-// stage st+2) are loaded at the very end and first used after the closing
+// The scalars of the next stage (src3: stage st+3, T_n: the width row of
+// stage st+1) are loaded at the very end and first used after the closing
 // barrier, whose wait covers them: scalar loads return out of order, so
-// while one is outstanding every wait for an operand read would have to
-// drain all of them.
+// while one is outstanding every wait for an operand read would drain all.
 __device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx& c, int st, int S,
-                                           const uint16_t* rd_w, const uint16_t* rd_x, uint16_t* wr_w,
-                                           uint16_t* wr_x, const WRegs& Wn, WRegs& Wf, u4v (&xr)[8],
-                                           const StageSrc& src, const DqRow& T, StageSrc& src_n, DqRow& T_n,
-                                           Frags& carry, Frags& other, f16v (&acc)[4][4]) {
-    issue_w(L, c, src, Wf);
+                                           const uint16_t* rd_x, uint16_t* wr_x, const QRegs (&Wc)[2],
+                                           QRegs (&Wn)[2], u4v (&xr)[8], const StageSrc& src1,
+                                           const StageSrc& src2, const DqRow& T, StageSrc& src3, DqRow& T_n,
+                                           Ops& carry, Ops& other, f16v (&acc)[2][8]) {
+    issue_w(L, c, src1, Wn);
     static_for<0, 4>([&](auto KC) {
         constexpr int KK = decltype(KC)::value;
-        Frags& rd = (KK & 1) ? carry : other;     // K-step KK lands here
-        Frags& mul = (KK & 1) ? other : carry;    // K-step KK - 1 (previous stage's 3 for KK = 0)
-        load_frags(rd_w, rd_x, c, KK, rd);
-        dequant_part<KK>(Wn, T, wr_w + c.tid * kPLd);
+        Ops& rd = (KK & 1) ? carry : other;     // K-step KK lands here
+        Ops& mul = (KK & 1) ? other : carry;    // K-step KK - 1 (previous stage's 3 for KK = 0)
+        load_x_ops(rd_x, c, KK, rd);
+        rd.a[0] = dequant_operand<KK>(Wc[0], T);
+        rd.a[1] = dequant_operand<KK>(Wc[1], T);
         store_x_chunk(xr[2 * KK], wr_x, c.tid, 2 * KK);
         store_x_chunk(xr[2 * KK + 1], wr_x, c.tid, 2 * KK + 1);
-        xr[2 * KK] = issue_x(L, c, src, 2 * KK);
-        xr[2 * KK + 1] = issue_x(L, c, src, 2 * KK + 1);
-        mfma_frags(mul, acc);
+        xr[2 * KK] = issue_x(L, c, src2, 2 * KK);
+        xr[2 * KK + 1] = issue_x(L, c, src2, 2 * KK + 1);
+        mfma_ops(mul, acc);
         region_schedule();
         __builtin_amdgcn_sched_barrier(0);
     });
     // Last, so that no wait inside the regions has a scalar load to cover.
-    src_n = stage_src(L, st + 3, S);
-    T_n = kDq[src.b];
+    src3 = stage_src(L, st + 3, S);
+    T_n = kDq[src1.b];
 }
 
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, int row_tiles, int col_tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t sw0[kPT * kPLd];
-    __shared__ __attribute__((aligned(16))) uint16_t sw1[kPT * kPLd];
     __shared__ __attribute__((aligned(16))) uint16_t sx0[kPT * kPLd];
     __shared__ __attribute__((aligned(16))) uint16_t sx1[kPT * kPLd];
 
@@ -299,40 +292,37 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, 
     PrefillCtx c;
     c.tid = threadIdx.x;
     c.lane = c.tid & 63;
-    const int wave = c.tid >> 6;
-    c.wn0 = (wave & 1) * 128;
-    c.wm0 = (wave >> 1) * 128;
-    c.n = (uint32_t)(n0 + c.tid);
-    c.n_ok = (int)c.n < L.N;
+    c.wave = c.tid >> 6;
+    c.q = (uint32_t)(c.lane >> 5);
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) c.col[ib] = (uint32_t)min(n0 + 64 * c.wave + 32 * ib + (c.lane & 31), L.N - 1);
     c.rw = buffer_rsrc(L.qweight, L.qbytes);
     c.rs = buffer_rsrc(L.scales, L.sbytes);
     const int rows = min(M - m0, kPT);
     c.rx = buffer_rsrc(L.x + (size_t)m0 * L.K, 2u * (uint32_t)rows * (uint32_t)L.K);
 
     const int S = 2 * L.G;
-    f16v acc[4][4];
+    f16v acc[2][8];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+    for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
+        for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[ib][jb][e] = 0.f;
 
-    WRegs W0, W1;
+    QRegs W0[2], W1[2];
     u4v xr[8];
-    StageSrc srcA, srcB;   // stage st+2 for the even / odd stage of an iteration
-    DqRow TA, TB;          // width row of stage st+1, likewise
+    StageSrc s1, s2;
+    DqRow T0;
     {
-        // Stage 0 is staged alone; from then on every stage stages the next.
-        const StageSrc s0 = stage_src(L, 0, S), s1 = stage_src(L, 1, S);
-        srcA = stage_src(L, 2, S);
-        TA = kDq[s1.b];
+        // Stage 0's x tile is staged alone; from then on every stage stages the next.
+        const StageSrc s0 = stage_src(L, 0, S);
+        s1 = stage_src(L, 1, S);
+        s2 = stage_src(L, 2, S);
+        T0 = kDq[s0.b];
         issue_w(L, c, s0, W0);
-        issue_w(L, c, s1, W1);
 #pragma unroll
         for (int it = 0; it < 8; ++it) xr[it] = issue_x(L, c, s0, it);
-        const DqRow& T0 = kDq[s0.b];
-        static_for<0, 4>([&](auto KC) { dequant_part<decltype(KC)::value>(W0, T0, sw0 + c.tid * kPLd); });
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
             store_x_chunk(xr[it], sx0, c.tid, it);
@@ -340,33 +330,37 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, 
         }
     }
     // Zero operands: the first stage's region 0 adds exact zeros.
-    Frags carry, other;
+    Ops carry, other;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        carry.a[i] = h8{};
-        carry.b[i] = h8{};
-    }
+    for (int k = 0; k < 8; ++k) carry.x[k] = h8{};
+    carry.a[0] = h8{};
+    carry.a[1] = h8{};
     __syncthreads();
     for (int st = 0; st < S; st += 2) {
-        stage_body(L, c, st, S, sw0, sx0, sw1, sx1, W1, W0, xr, srcA, TA, srcB, TB, carry, other, acc);
+        StageSrc s3, s4;
+        DqRow T1, T2;
+        stage_body(L, c, st, S, sx0, sx1, W0, W1, xr, s1, s2, T0, s3, T1, carry, other, acc);
         __syncthreads();
-        stage_body(L, c, st + 1, S, sw1, sx1, sw0, sx0, W0, W1, xr, srcB, TB, srcA, TA, carry, other, acc);
+        stage_body(L, c, st + 1, S, sx1, sx0, W1, W0, xr, s2, s3, T1, s4, T2, carry, other, acc);
         __syncthreads();
+        s1 = s3;
+        s2 = s4;
+        T0 = T2;
     }
-    mfma_frags(carry, acc);
+    mfma_ops(carry, acc);
 
     // Epilogue: lane holds rows m = 32 jb + lane % 32 and, per a, four
-    // consecutive columns n = 32 ib + 8 a + 4 (lane / 32) + [0, 4).
+    // consecutive columns n = 64 wave + 32 ib + 8 a + 4 (lane / 32) + [0, 4).
     const int lr = c.lane & 31, lh = c.lane >> 5;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-        const int m = m0 + c.wm0 + 32 * jb + lr;
+    for (int jb = 0; jb < 8; ++jb) {
+        const int m = m0 + 32 * jb + lr;
         if (m >= M) continue;
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
+        for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const int n = n0 + c.wn0 + 32 * ib + 8 * a + 4 * lh;
+                const int n = n0 + 64 * c.wave + 32 * ib + 8 * a + 4 * lh;
                 if (n >= L.N) continue;
                 const uint32_t lo = (uint32_t)f32_to_f16_bits(acc[ib][jb][4 * a]) |
                                     ((uint32_t)f32_to_f16_bits(acc[ib][jb][4 * a + 1]) << 16);

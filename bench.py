@@ -8,9 +8,11 @@ exq plan launch.  Inputs are seeded synthetic tensors of the model's shapes
 
 Prints one JSON line: whole-step HBM throughput (algorithmic bytes / step
 time), ms/step, the decode kernel's roofline and the CPU oracle timed on a
-bounded sample of the same workload.
+bounded sample of the same workload.  A second leg ("prefill") times the
+prefill path on the same seven 70B shapes at M = 2048 tokens (mixed 4.0 bpw
+from {3,4,5,6}) against the fp16 matrix-core peak.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 5|3] [--m 1]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 5|3] [--m 1] [--no-prefill]
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_plan_70b_m1_counters.json")
 
 
@@ -37,7 +40,7 @@ def log(msg):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("exq_device.hip", "exq_internal.h"):
+    for f in ("exq_device.hip", "exq_device_common.h", "exq_internal.h"):
         with open(os.path.join(ROOT, "mixed_bitrate_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -77,24 +80,93 @@ def omp_threads() -> int:
         return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(kept, M, gpu_ys):
+def cpu_baseline(kept, M, gpu_ys, min_seconds):
     """Time the CPU oracle (as it stands) on the kept linears: its own quantize+pack
     (untimed), then the timed path from packed storage -- bit-by-bit unpack,
-    dequantize, fp64 matmul -- over every output column."""
+    dequantize, fp64 matmul -- over every output column, repeated over the
+    sample until at least `min_seconds` of timed work."""
     import oracle
     from synth import workloads
-    secs, nbytes, worst = 0.0, 0, 0.0
+    prepared = []
+    worst = 0.0
     for (spec, W, widths), y_gpu in zip(kept, gpu_ys):
         _, s_ref, q_ref = oracle.reference_layer(W, widths)
-        x = workloads.make_x(spec, M)
-        cols = np.arange(spec.N, dtype=np.int64)
-        t0 = time.perf_counter()
-        y_ref, bnd = oracle.gemm_packed_cols(x, q_ref, s_ref, widths, spec.K, spec.N, cols)
-        secs += time.perf_counter() - t0
-        nbytes += workloads.algorithmic_bytes(spec.K, spec.N, widths, M)
-        _, w = oracle.within_tolerance(y_gpu.astype(np.float64), y_ref, bnd)
-        worst = max(worst, w)
-    return secs, nbytes, worst
+        prepared.append((spec, widths, s_ref, q_ref, workloads.make_x(spec, M), y_gpu))
+    secs, nbytes, reps = 0.0, 0, 0
+    while reps == 0 or secs < min_seconds:
+        for spec, widths, s_ref, q_ref, x, y_gpu in prepared:
+            cols = np.arange(spec.N, dtype=np.int64)
+            t0 = time.perf_counter()
+            y_ref, bnd = oracle.gemm_packed_cols(x, q_ref, s_ref, widths, spec.K, spec.N, cols)
+            secs += time.perf_counter() - t0
+            nbytes += workloads.algorithmic_bytes(spec.K, spec.N, widths, M)
+            if reps == 0:
+                _, w = oracle.within_tolerance(y_gpu.astype(np.float64), y_ref, bnd)
+                worst = max(worst, w)
+        reps += 1
+    return secs, nbytes, worst, reps
+
+
+def prefill_leg(exq, torch, steps, warmup):
+    """The seven 70B-shaped linears at M = 2048 (mixed 4.0 bpw), one exq_gemm
+    call each per step; step time and the prefill kernel's average launch time."""
+    from synth import workloads
+    M = workloads.M_VALUES[4][0]
+    specs = workloads.linears(4)
+    layers, xs, ys, _, _ = build_stack(exq, torch, specs, M)
+    flops = sum(2 * M * sp.K * sp.N for sp in specs)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for l, x, y in zip(layers, xs, ys):
+            exq.exq_gemm(x.data_ptr(), M, l.handle, y.data_ptr(), stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+          for _ in range(steps)]
+    for k in range(steps):
+        for (a, b), l, x, y in zip(ev[k], layers, xs, ys):
+            a.record(stream)
+            exq.exq_gemm(x.data_ptr(), M, l.handle, y.data_ptr(), stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])
+    kernel_ms_per_step = float(launch_ms.sum(axis=1).mean())
+    for l in layers:
+        l.close()
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms_per_step * 1e-3) / 1e12
+    log("prefill step %.3f ms, %.1f TFLOP/s; kernels %.3f ms (%.1f TFLOP/s)" % (ms_step, tflops, kernel_ms_per_step, achieved))
+    return {
+        "workload": "llama3-70b-shaped block (7 linears), mixed 4.0 bpw {3,4,5,6}, M=%d tokens" % M,
+        "metric": "prefill TFLOP/s (7 exq_gemm calls per step)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(ms_step, 4),
+        "steps": steps,
+        "warmup": warmup,
+        "flops_per_step": flops,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "prefill_kernel (one launch per linear)",
+            "flops_per_step": flops,
+            "kernel_ms_per_step": round(kernel_ms_per_step, 4),
+        },
+    }
 
 
 def main():
@@ -107,6 +179,9 @@ def main():
     ap.add_argument("--blocks", type=int, default=None, help="limit the number of 70B blocks (config 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=1, help="blocks of the workload the oracle is timed on")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum timed oracle work (the sample is repeated)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the M = 2048 prefill leg")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--variants", action="store_true", help="also time per-linear calls, ungraphed and graphed")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="run a plain device copy of this size (for counter calibration) and exit")
@@ -224,17 +299,28 @@ def main():
     if kept:
         log("timing the CPU oracle on %d linears" % len(kept))
         gpu_ys = [ys[i].cpu().numpy() for i in range(len(kept))]
-        secs, cbytes, worst = cpu_baseline(kept, M, gpu_ys)
+        secs, cbytes, worst, reps = cpu_baseline(kept, M, gpu_ys, args.cpu_seconds)
         cpu = {
             "value": round(cbytes / secs / 1e9, 4),
             "unit": "GB/s",
             "cores": omp_threads(),
             "kind": "oracle",
-            "sample": "%d linears (block%s 0..%d of the same stack) at M=%d, every output column: bit-by-bit "
-                      "unpack + dequant + fp64 matmul from the oracle's own packed layer; %.1f s for %.2f GB; "
-                      "worst GPU error / tolerance on the sample %.3f" % (len(kept), "s" if args.cpu_blocks > 1 else "",
-                                                                         args.cpu_blocks - 1, M, secs, cbytes / 1e9, worst),
+            "sample": "%d linears (block%s 0..%d of the same stack) at M=%d, every output column, %d passes: "
+                      "bit-by-bit unpack + dequant + fp64 matmul from the oracle's own packed layer; %.1f s for "
+                      "%.2f GB; worst GPU error / tolerance on the sample %.3f" % (
+                          len(kept), "s" if args.cpu_blocks > 1 else "", args.cpu_blocks - 1, M, reps, secs,
+                          cbytes / 1e9, worst),
         }
+
+    prefill = None
+    if not args.no_prefill:
+        for p in plans:
+            p.close()
+        for l in layers:
+            l.close()
+        del layers, xs, ys, plans
+        torch.cuda.empty_cache()
+        prefill = prefill_leg(exq, torch, args.prefill_steps, 2)
 
     out = {
         "metric": "quant GEMV eff. HBM GB/s (% peak) + ms/step, 70B-shaped 2.55bpw M=" + str(M),
@@ -270,6 +356,7 @@ def main():
             "avg_launch_us": round(kernel_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,
+        "prefill": prefill,
     }
     out.update(extra)
     print(json.dumps(out))

@@ -35,6 +35,14 @@ def _load():
     if not os.path.exists(LIB_PATH):
         from . import build as _b
         _b.build()
+    # PyTorch ships its own HIP runtime.  Importing it first makes libexq bind
+    # to that already-loaded runtime instead of loading a second copy from
+    # the ROCm install, so device pointers and streams from torch and from
+    # libexq belong to one runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.exq_status_string.argtypes = [i32]

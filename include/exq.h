@@ -127,19 +127,23 @@ exq_status exq_dequant(exq_layer_t layer, void* w_out, void* stream);
 
 /* ------------------------------------------------------- batched launches */
 
-/* Bind a list of independent linears into one launch (for a decode step:
- * the pages' fused kernels cut launch overhead at small batch, per the
- * ainews.cool exllamav3 article, section "technical deep dive").
+/* Bind a list of independent linears into one launch (the pages' fused
+ * kernels cut launch overhead at small batch, per the ainews.cool exllamav3
+ * article, section "technical deep dive"; at large batch one launch also
+ * lets the small linears fill the machine beside the large ones).
  *   count   number of linears, >= 1
  *   layers  host array of handles (borrowed; must outlive the plan)
  *   xs, ys  host arrays of device pointers, fp16 [M][K_i] and [M][N_i]
- *   M       1..16, the same for every linear
+ *   M       >= 1, the same for every linear.  M <= 16: decode plan (column
+ *           tiles of every linear, longest K first).  M > 16: prefill plan
+ *           (256 x 256 output tiles of every linear, longest K first).
  * A plan owns a small device copy of these descriptors; buffers are bound at
  * creation, like a captured graph.  exq_plan_run computes every y_i =
  * x_i * W_i^T in one kernel launch, deterministically and to the same
  * accuracy bound as exq_gemm (its tiling, hence its summation order, may
  * differ from a single exq_gemm call).
- * Outputs must not overlap any input or each other. */
+ * Outputs must not overlap any input or each other.  Errors: INVALID_ARG,
+ * UNSUPPORTED (more than 65535 linears or tiles of one linear), OOM, HIP. */
 exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* const* xs,
                            const void* const* ys, int M, exq_plan_t* out);
 exq_status exq_plan_run(exq_plan_t plan, void* stream);

@@ -279,7 +279,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_plan_kernel(const LinearDe
         const EXQ_GLOBAL uint32_t* src = gptr<uint32_t>(list + (e & 0xFFFFu));
         uint32_t* dst = reinterpret_cast<uint32_t*>(&L);
 #pragma unroll
-        for (int i = 0; i < (int)(sizeof(LinearDev) / 4); ++i) dst[i] = src[i];
+        for (int i = 0; i < (int)(sizeof(LinearDev) / 4); ++i)
+            dst[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)src[i]);   // uniform: SGPRs
     }
     decode_wg<MB, 64, M1>(L, (int)(e >> 16), M, red);
 }
@@ -337,8 +338,12 @@ __global__ __launch_bounds__(64) void dequant_kernel(LinearDev L, uint16_t* __re
 using namespace exq;
 
 
+constexpr int kXcds = 8;                     // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr uint32_t kPlanEmpty = 0xFFFFFFFFu;  // prefill plan entry of a workgroup with no tile
+
 struct exq_plan {
     int count = 0, M = 1, total_wgs = 0;
+    bool prefill = false;   // M > 16: prefill tiles, else decode column tiles
     LinearDev* d_list = nullptr;
     uint32_t* d_wg_map = nullptr;
 };
@@ -432,6 +437,9 @@ void launch_plan(const exq_plan* P, hipStream_t s) {
 }  // namespace
 
 extern exq_status exq_prefill_launch(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream);
+extern int exq_prefill_tiles(const exq_layer* L, int M);
+extern exq_status exq_prefill_plan_launch(const LinearDev* d_list, const uint32_t* d_wg_map, int total_wgs, int M,
+                                          hipStream_t stream);
 
 // Decode kernel over consecutive slices of at most 16 rows of x (any M).
 exq_status exq_decode_rows(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream) {
@@ -531,7 +539,8 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
     if (!out) return fail(EXQ_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     if (count < 1 || !layers || !xs || !ys) return fail(EXQ_ERR_INVALID_ARG, "empty or NULL plan arrays");
-    if (M < 1 || M > kMaxDecodeM) return fail(EXQ_ERR_INVALID_ARG, "plan M=%d must be in [1, 16]", M);
+    if (M < 1) return fail(EXQ_ERR_INVALID_ARG, "plan M=%d must be >= 1", M);
+    const bool prefill = M > kMaxDecodeM;
     if (count > 65535) return fail(EXQ_ERR_UNSUPPORTED, "plan of %d linears (at most 65535)", count);
     for (int i = 0; i < count; ++i)
         if (!layers[i] || !xs[i] || !ys[i]) return fail(EXQ_ERR_INVALID_ARG, "plan entry %d is NULL", i);
@@ -547,10 +556,16 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
                 return fail(EXQ_ERR_INVALID_ARG, "outputs %d and %d overlap", i, j);
         }
         list[i] = linear_dev(L, xs[i], const_cast<void*>(ys[i]));
-        list[i].tiles = L->N / 64;
-        int words = 0;
-        for (int g = 0; g < L->G; ++g) words += L->widths[g];
-        work[i] = words + L->G;   // per-workgroup cost, as in the wave plan
+        if (prefill) {
+            list[i].tiles = exq_prefill_tiles(L, M);
+            if (list[i].tiles == 0) return fail(EXQ_ERR_UNSUPPORTED, "entry %d: K or M too large for a prefill plan", i);
+            work[i] = L->K;   // per-workgroup cost: one tile over all of K
+        } else {
+            list[i].tiles = L->N / 64;
+            int words = 0;
+            for (int g = 0; g < L->G; ++g) words += L->widths[g];
+            work[i] = words + L->G;   // per-workgroup cost, as in the wave plan
+        }
     }
     // Longest workgroups first, so the launch does not end on a tail of
     // long-K tiles; within a linear, tiles in order.
@@ -558,8 +573,31 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
     for (int i = 0; i < count; ++i) byw[i] = i;
     std::stable_sort(byw.begin(), byw.end(), [&](int a, int b) { return work[a] > work[b]; });
     std::vector<uint32_t> wg_map;
-    for (int i : byw)
-        for (int t = 0; t < list[i].tiles; ++t) wg_map.push_back((uint32_t)i | ((uint32_t)t << 16));
+    if (!prefill) {
+        for (int i : byw)
+            for (int t = 0; t < list[i].tiles; ++t) wg_map.push_back((uint32_t)i | ((uint32_t)t << 16));
+    } else {
+        // Workgroup ids are dispatched to the 8 XCDs round-robin (id % 8).  Each
+        // row tile of a linear goes, whole, to the least-loaded XCD, so its
+        // column tiles share that XCD's L2 for x; entry i is then the next
+        // tile queued for XCD i % 8, and short queues are padded with empty
+        // entries (kPlanEmpty: the workgroup exits at once).
+        std::vector<std::vector<uint32_t>> queue(kXcds);
+        std::vector<long> load(kXcds, 0);
+        for (int i : byw) {
+            const int col_tiles = (layers[i]->N + 255) / 256, row_tiles = list[i].tiles / col_tiles;
+            for (int r = 0; r < row_tiles; ++r) {
+                const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+                for (int ct = 0; ct < col_tiles; ++ct)
+                    queue[x].push_back((uint32_t)i | ((uint32_t)(r * col_tiles + ct) << 16));
+                load[x] += (long)col_tiles * work[i];
+            }
+        }
+        size_t longest = 0;
+        for (const auto& q : queue) longest = std::max(longest, q.size());
+        for (size_t k = 0; k < longest; ++k)
+            for (int x = 0; x < kXcds; ++x) wg_map.push_back(k < queue[x].size() ? queue[x][k] : kPlanEmpty);
+    }
     if (wg_map.size() > (size_t)INT32_MAX) return fail(EXQ_ERR_UNSUPPORTED, "plan too large");
     for (int i = 0; i < count; ++i)
         if (list[i].tiles >= 65536) return fail(EXQ_ERR_UNSUPPORTED, "entry %d has too many tiles", i);
@@ -567,6 +605,7 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
     if (!P) return fail(EXQ_ERR_OOM, "host allocation");
     P->count = count;
     P->M = M;
+    P->prefill = prefill;
     P->total_wgs = (int)wg_map.size();
     hipError_t e;
     if ((e = hipMalloc(&P->d_list, sizeof(LinearDev) * count)) != hipSuccess ||
@@ -586,6 +625,7 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
 
 exq_status exq_plan_run(exq_plan_t P, void* stream) {
     if (!P) return fail(EXQ_ERR_INVALID_ARG, "plan is NULL");
+    if (P->prefill) return exq_prefill_plan_launch(P->d_list, P->d_wg_map, P->total_wgs, P->M, static_cast<hipStream_t>(stream));
     launch_plan(P, static_cast<hipStream_t>(stream));
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? EXQ_OK : hip_fail(e, "plan launch");

@@ -279,16 +279,9 @@ __device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx&
     T_n = kDq[src1.b];
 }
 
-__global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, int row_tiles, int col_tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t sx0[kPT * kPLd];
-    __shared__ __attribute__((aligned(16))) uint16_t sx1[kPT * kPLd];
-
-    // XCD-aware tile order: ids i, i+8, i+16, ... (one XCD) take consecutive tiles.
-    const int T = row_tiles * col_tiles;
-    const int i = blockIdx.x, xcd = i & 7, per = T >> 3, rem = T & 7;
-    const int t = xcd * per + min(xcd, rem) + (i >> 3);
-    const int m0 = (t / col_tiles) * kPT, n0 = (t % col_tiles) * kPT;
-
+// One 256 x 256 output tile (rows m0.., columns n0..) over all of K.
+__device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, int n0, uint16_t* sx0,
+                                             uint16_t* sx1) {
     PrefillCtx c;
     c.tid = threadIdx.x;
     c.lane = c.tid & 63;
@@ -372,6 +365,38 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, 
     }
 }
 
+__global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, int row_tiles, int col_tiles) {
+    __shared__ __attribute__((aligned(16))) uint16_t sx0[kPT * kPLd];
+    __shared__ __attribute__((aligned(16))) uint16_t sx1[kPT * kPLd];
+    // XCD-aware tile order: ids i, i+8, i+16, ... (one XCD) take consecutive tiles.
+    const int T = row_tiles * col_tiles;
+    const int i = blockIdx.x, xcd = i & 7, per = T >> 3, rem = T & 7;
+    const int t = xcd * per + min(xcd, rem) + (i >> 3);
+    prefill_tile(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sx0, sx1);
+}
+
+// Several linears in one launch: workgroup i takes entry i of wg_map
+// (linear | tile << 16, tiles numbered row-major, or all ones: no tile); the
+// host orders the map longest-K first and XCD-aware.
+__global__ __launch_bounds__(kPThreads) void prefill_plan_kernel(const LinearDev* __restrict__ list,
+                                                                  const uint32_t* __restrict__ wg_map, int M) {
+    __shared__ __attribute__((aligned(16))) uint16_t sx0[kPT * kPLd];
+    __shared__ __attribute__((aligned(16))) uint16_t sx1[kPT * kPLd];
+    const uint32_t e = gptr<uint32_t>(wg_map)[blockIdx.x];
+    if (e == 0xFFFFFFFFu) return;   // padding entry: no tile
+    LinearDev L;
+    {
+        static_assert(sizeof(LinearDev) % 4 == 0, "descriptor copy");
+        const EXQ_GLOBAL uint32_t* src = gptr<uint32_t>(list + (e & 0xFFFFu));
+        uint32_t* dst = reinterpret_cast<uint32_t*>(&L);
+#pragma unroll
+        for (int k = 0; k < (int)(sizeof(LinearDev) / 4); ++k)
+            dst[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)src[k]);   // uniform: SGPRs
+    }
+    const int col_tiles = (L.N + kPT - 1) / kPT, t = (int)(e >> 16);
+    prefill_tile(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sx0, sx1);
+}
+
 }  // namespace
 }  // namespace exq
 
@@ -388,4 +413,18 @@ exq_status exq_prefill_launch(const exq_layer* L, const void* x, int M, void* y,
                        (int)row_tiles, (int)col_tiles);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? EXQ_OK : fail(EXQ_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+}
+
+// Tiles of one linear in a prefill plan (0 if the linear cannot be planned).
+int exq_prefill_tiles(const exq_layer* L, int M) {
+    if ((size_t)2 * kPT * (size_t)L->K >= (size_t)kBufOOB) return 0;
+    const long t = (long)((M + kPT - 1) / kPT) * ((L->N + kPT - 1) / kPT);
+    return t < 65536 ? (int)t : 0;
+}
+
+exq_status exq_prefill_plan_launch(const LinearDev* d_list, const uint32_t* d_wg_map, int total_wgs, int M,
+                                   hipStream_t stream) {
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3((unsigned)total_wgs), dim3(kPThreads), 0, stream, d_list, d_wg_map, M);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? EXQ_OK : fail(EXQ_ERR_HIP, "prefill plan launch: %s", hipGetErrorString(e));
 }

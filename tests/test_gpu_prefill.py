@@ -138,3 +138,31 @@ def test_long_k(exq):
     y_ref, bnd = oracle.gemm(x, w_ref)
     assert_within(y, y_ref, bnd, "prefill K=%d" % K)
     layer.close()
+
+
+def test_prefill_plan_matches_oracle_and_is_repeatable(exq):
+    """Several linears, different K and N, one launch at M > 16."""
+    specs = [(384, 320, [3, 4, 5]), (1024, 128, [2] * 6 + [8, 6]), (256, 512, [6, 2])]
+    layers, refs = [], []
+    for i, (K, N, widths) in enumerate(specs):
+        W = synth.weight(synth.seed_for("pf-plan", i), N, K)
+        layer, w_ref = make_layer(exq, W, widths)
+        layers.append(layer)
+        refs.append(w_ref)
+    for M in (17, 300):
+        xs_h = [synth.activations(synth.seed_for("pf-plan-x", i, M), M, l.K) for i, l in enumerate(layers)]
+        xs = [to_dev(x) for x in xs_h]
+        ys = [torch.empty((M, l.N), dtype=torch.float16, device="cuda") for l in layers]
+        note("prefill plan M=%d" % M)
+        plan = exq.Plan(layers, xs, ys, M)
+        plan.run()
+        got = [y_to_np(y).copy() for y in ys]
+        for x, g, w_ref, l in zip(xs_h, got, refs, layers):
+            y_ref, bnd = oracle.gemm(x, w_ref)
+            assert_within(g, y_ref, bnd, "prefill plan M=%d N=%d" % (M, l.N))
+        plan.run()
+        for y, g in zip(ys, got):
+            np.testing.assert_array_equal(y_to_np(y), g)
+        plan.close()
+    for l in layers:
+        l.close()

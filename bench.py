@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_plan_70b_m1_counters.json")
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_plan_70b_m2048_counters.json")
 
 
 def log(msg):
@@ -38,9 +39,9 @@ def log(msg):
     sys.stderr.flush()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=("exq_device.hip", "exq_device_common.h", "exq_internal.h")) -> str:
     h = hashlib.sha256()
-    for f in ("exq_device.hip", "exq_device_common.h", "exq_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "mixed_bitrate_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -149,6 +150,12 @@ def prefill_leg(exq, torch, steps, warmup):
         l.close()
     tflops = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(PREFILL_COUNTERS):
+        with open(PREFILL_COUNTERS) as f:
+            prof = json.load(f)
+        if prof.get("kernel_source_hash") == kernel_source_hash(("exq_prefill.hip", "exq_device_common.h", "exq_internal.h")):
+            traffic = prof.get("hbm_bytes_per_launch")
     log("prefill step %.3f ms, %.1f TFLOP/s; launch %.3f ms (%.1f TFLOP/s); 7 calls %.3f ms" % (
         ms_step, tflops, kernel_ms, achieved, ms_calls))
     return {
@@ -167,7 +174,7 @@ def prefill_leg(exq, torch, steps, warmup):
             "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "kernel": "prefill_plan_kernel (one launch = the block's 7 linears)",
             "flops_per_launch": flops,
             "avg_launch_ms": round(kernel_ms, 4),

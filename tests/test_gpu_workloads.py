@@ -84,3 +84,34 @@ CFG5_SAMPLE = (0, 6, 37 * 7 + 4, 79 * 7 + 1)
 def test_cfg5_stack_sample(exq, idx):
     spec = workloads.linears(5)[idx]
     check_linear(exq, spec, workloads.M_VALUES[5], ncols=128, dequant=False)
+
+
+def test_cfg5_every_linear(exq):
+    """Configuration 5 in full: every one of the 560 linears at M = 1 and a
+    seeded sample of 40 at M = 16, each on a column sample whose reference the
+    oracle derives from W itself (its own quantizer, dequantization and fp64
+    matmul on those columns: the quantizer works per (group, column))."""
+    specs = workloads.linears(5)
+    m16 = set(np.random.default_rng(5016).choice(len(specs), 40, replace=False).tolist())
+    wbuf = None
+    worst = 0.0
+    for i, spec in enumerate(specs):
+        if i % 70 == 0:
+            note("cfg5 sweep: linear %d/%d" % (i, len(specs)))
+        if wbuf is None or wbuf.size < spec.N * spec.K:
+            wbuf = np.empty(spec.N * spec.K, dtype=np.float32)
+        W = wbuf[: spec.N * spec.K].reshape(spec.N, spec.K)
+        workloads.make_weight(spec, out=W)
+        widths = workloads.make_widths(spec, W)
+        q, s = exq.exq_pack(W, widths)
+        layer = exq.Layer(spec.K, spec.N, widths, q, s)
+        cols = sample_cols(spec.N, 24, spec.w_seed() & 0xFFFF)
+        codes_c, scales_c = oracle.quantize(W[cols], widths)
+        w_ref = oracle.dequant(codes_c, scales_c, widths)
+        for M in ((1, 16) if i in m16 else (1,)):
+            x = workloads.make_x(spec, M)
+            y = y_to_np(layer.gemm(to_dev(x)))
+            y_ref, bnd = oracle.gemm(x, w_ref)
+            worst = max(worst, assert_within(y[:, cols], y_ref, bnd, "cfg5 %s M=%d" % (spec.name, M)))
+        layer.close()
+    note("cfg5 sweep done, worst error / tolerance %.3f" % worst)

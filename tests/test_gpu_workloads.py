@@ -115,3 +115,32 @@ def test_cfg5_every_linear(exq):
             worst = max(worst, assert_within(y[:, cols], y_ref, bnd, "cfg5 %s M=%d" % (spec.name, M)))
         layer.close()
     note("cfg5 sweep done, worst error / tolerance %.3f" % worst)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_cfg3_block_as_one_plan(exq, M):
+    """The seven linears of a 70B-shaped block as one decode plan (the launch
+    bench.py times), each checked on a column sample against the oracle."""
+    specs = workloads.linears(3)
+    layers, refs, xs_h = [], [], []
+    for spec in specs:
+        W = workloads.make_weight(spec)
+        widths = workloads.make_widths(spec, W)
+        q, s = exq.exq_pack(W, widths)
+        cols = sample_cols(spec.N, 48, spec.w_seed() & 0xFFFF)
+        codes_c, scales_c = oracle.quantize(W[cols], widths)
+        refs.append((cols, oracle.dequant(codes_c, scales_c, widths)))
+        layers.append(exq.Layer(spec.K, spec.N, widths, q, s))
+        xs_h.append(workloads.make_x(spec, M))
+        del W
+    xs = [to_dev(x) for x in xs_h]
+    ys = [torch.empty((M, l.N), dtype=torch.float16, device="cuda") for l in layers]
+    note("cfg3 block plan M=%d" % M)
+    plan = exq.Plan(layers, xs, ys, M)
+    plan.run()
+    for spec, x, y, (cols, w_ref) in zip(specs, xs_h, ys, refs):
+        y_ref, bnd = oracle.gemm(x, w_ref)
+        assert_within(y_to_np(y)[:, cols], y_ref, bnd, "cfg3 plan %s M=%d" % (spec.name, M))
+    plan.close()
+    for l in layers:
+        l.close()

@@ -34,6 +34,18 @@ PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_plan_70b_m1_counters.j
 PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_plan_70b_m2048_counters.json")
 
 
+STREAM_READ_WGS = 8192   # workgroups of the streaming-read diagnostic (about 35 KB each per 286 MB)
+
+
+def trimmed_mean(samples) -> float:
+    """Mean of the samples that lie between the 5/16 and 11/16 quantiles
+    (the middle three eighths of the sorted list)."""
+    s = np.sort(np.asarray(samples, dtype=np.float64))
+    n = len(s)
+    lo, hi = (5 * n) // 16, max((11 * n + 15) // 16, (5 * n) // 16 + 1)
+    return float(s[lo:hi].mean())
+
+
 def log(msg):
     sys.stderr.write("[bench] %s\n" % msg)
     sys.stderr.flush()
@@ -196,6 +208,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the M = 2048 prefill leg")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--variants", action="store_true", help="also time per-linear calls, ungraphed and graphed")
+    ap.add_argument("--no-stream-read", action="store_true", help="skip the plain streaming-read ceiling")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="run a plain device copy of this size (for counter calibration) and exit")
     args = ap.parse_args()
@@ -268,6 +281,71 @@ def main():
     bytes_per_launch = step_bytes / nblk
     achieved = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
     log("step %.3f ms, %.1f GB/s; decode launch %.1f us (%.1f GB/s)" % (ms_step, gbs, kernel_ms * 1e3, achieved))
+
+    # Per-step durations (an event pair around every step, a third pass) for
+    # the median and the trimmed mean of the 5/16-11/16 quantiles.
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in step_ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in step_ev])
+    step_stats = {"median_ms": round(float(np.median(per_step)), 4),
+                  "trimmed_mean_ms": round(trimmed_mean(per_step), 4),
+                  "min_ms": round(float(per_step.min()), 4), "max_ms": round(float(per_step.max()), 4),
+                  "trimmed_mean": "mean of the per-step times between the 5/16 and 11/16 quantiles"}
+
+    # The same step captured once as a HIP graph and replayed.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
+        for p in plans:
+            p.run(cap)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_graphed = g0.elapsed_time(g1) / args.steps
+    del graph
+
+    # Diagnostic ceiling: a plain streaming read of the same bytes, one launch
+    # per block (cold: 16 windows rotate through HBM), same step structure.
+    read = None
+    if not args.no_stream_read:
+        win = (int(bytes_per_launch) // 16) * 16
+        copies = 16
+        rbuf = torch.empty(copies * win // 4, dtype=torch.int32, device="cuda").fill_(1)
+        sink = torch.zeros(STREAM_READ_WGS, dtype=torch.int32, device="cuda")
+        base = rbuf.data_ptr()
+
+        def read_step(s):
+            for b in range(nblk):
+                exq.exq_stream_read(base + ((s * nblk + b) % copies) * win, win, sink.data_ptr(), STREAM_READ_WGS,
+                                    stream)
+
+        for s in range(2):
+            read_step(s)
+        torch.cuda.synchronize()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for s in range(args.steps):
+            read_step(s)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        read_ms = r0.elapsed_time(r1) / args.steps
+        read_gbs = win * nblk / (read_ms * 1e-3) / 1e9
+        read = {"ms_per_step": round(read_ms, 4), "GB/s": round(read_gbs, 1),
+                "decode_pct_of_stream_read": round(100 * gbs / read_gbs, 1),
+                "kernel": "stream_read_kernel, %d workgroups per launch, %d B per launch" % (STREAM_READ_WGS, win)}
+        del rbuf, sink
+        torch.cuda.empty_cache()
+    log("graphed step %.3f ms; stream read %s" % (ms_step_graphed, read))
 
     traffic = None
     if os.path.exists(PROFILE_COUNTERS):
@@ -368,6 +446,9 @@ def main():
             "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": round(kernel_ms * 1e3, 3),
         },
+        "ms_per_step_graphed": round(ms_step_graphed, 4),
+        "step_stats": step_stats,
+        "stream_read": read,
         "cpu_baseline": cpu,
         "prefill": prefill,
     }

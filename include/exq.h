@@ -115,8 +115,9 @@ void exq_layer_destroy(exq_layer_t layer);
  *   x  device, fp16 [M][K] row-major, 16-byte aligned
  *   y  device, fp16 [M][N] row-major, 16-byte aligned, must not overlap x
  *   M >= 1.  M <= 16 uses the decode kernel (scale factored per group, MFMA
- *   accumulation); larger M uses the prefill kernel (fp16 W_hat tiles in LDS,
- *   MFMA).  Accumulation is fp32 in both; output is fp16 RNE.
+ *   accumulation); larger M uses the prefill kernel (W_hat decoded exactly
+ *   into fp16 MFMA operands, activation tiles in LDS).  Accumulation is fp32
+ *   in both; output is fp16 RNE.
  * Accuracy: |y - y_ref| <= 2e-3 * sum_k |x_k * w_hat_k| + 1e-5 per output,
  * y_ref the exact (fp64) product of the fp16 inputs. */
 exq_status exq_gemm(const void* x, int M, exq_layer_t layer, void* y, void* stream);
@@ -148,6 +149,20 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
                            const void* const* ys, int M, exq_plan_t* out);
 exq_status exq_plan_run(exq_plan_t plan, void* stream);
 void exq_plan_destroy(exq_plan_t plan);
+
+/* ------------------------------------------------------------ diagnostic */
+
+/* A plain streaming read, the practical HBM read ceiling that the decode
+ * kernel's rate is compared with (it streams with the same 1 KB wave loads,
+ * minus all decoding).  Workgroup w of sink_words reads the w-th of
+ * sink_words equal slices of buf (the last one clipped) and stores the XOR
+ * of every 32-bit word of its slice to sink[w]; the XOR of all of sink is
+ * therefore the XOR of the whole buffer.
+ *   buf         device, 16-byte aligned, bytes > 0 and a multiple of 16
+ *   sink        device uint32 [sink_words], 4-byte aligned, written
+ *   sink_words  1 .. 2^20, the number of workgroups
+ * Asynchronous on `stream`.  Errors: INVALID_ARG, HIP. */
+exq_status exq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int sink_words, void* stream);
 
 #ifdef __cplusplus
 }

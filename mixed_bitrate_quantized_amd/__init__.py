@@ -61,8 +61,9 @@ def _load():
     lib.exq_plan_run.argtypes = [vp, vp]
     lib.exq_plan_destroy.argtypes = [vp]
     lib.exq_plan_destroy.restype = None
+    lib.exq_stream_read.argtypes = [vp, u64, vp, i32, vp]
     for f in (lib.exq_pack, lib.exq_layer_create, lib.exq_gemm, lib.exq_dequant, lib.exq_plan_create,
-              lib.exq_plan_run):
+              lib.exq_plan_run, lib.exq_stream_read):
         f.restype = i32
     return lib
 
@@ -73,6 +74,7 @@ lib = _load()
 EXPORTED = (
     "exq_status_string", "exq_last_error", "exq_packed_bytes", "exq_pack", "exq_layer_create",
     "exq_layer_destroy", "exq_gemm", "exq_dequant", "exq_plan_create", "exq_plan_run", "exq_plan_destroy",
+    "exq_stream_read",
 )
 
 
@@ -156,6 +158,10 @@ def exq_plan_create(handles, x_ptrs, y_ptrs, M: int) -> int:
 
 def exq_plan_run(plan: int, stream=None) -> None:
     _check(lib.exq_plan_run(plan, _stream_ptr(stream)), "exq_plan_run")
+
+
+def exq_stream_read(buf_ptr: int, nbytes: int, sink_ptr: int, sink_words: int, stream=None) -> None:
+    _check(lib.exq_stream_read(buf_ptr, nbytes, sink_ptr, sink_words, _stream_ptr(stream)), "exq_stream_read")
 
 
 def exq_plan_destroy(plan: int) -> None:

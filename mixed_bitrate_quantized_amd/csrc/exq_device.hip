@@ -331,6 +331,43 @@ __global__ __launch_bounds__(64) void dequant_kernel(LinearDev L, uint16_t* __re
     }
 }
 
+// ---------------------------------------------------------------- diagnostic
+
+// Plain streaming read: workgroup w reads 16-byte words [w*chunk, (w+1)*chunk)
+// of `a` (clipped to n16) with non-temporal loads, four in flight per lane,
+// and stores the XOR of every 32-bit word it read to sink[w].  It has the
+// decode kernel's access unit (a 1 KB wave load) and no arithmetic, so its
+// rate is the read ceiling a weight-streaming kernel can reach.
+__global__ __launch_bounds__(512) void stream_read_kernel(const u4v* __restrict__ a, size_t n16, size_t chunk,
+                                                          uint32_t* __restrict__ sink) {
+    const size_t begin = (size_t)blockIdx.x * chunk;
+    const size_t end = begin < n16 ? (n16 - begin < chunk ? n16 : begin + chunk) : begin;
+    const EXQ_GLOBAL u4v* g = gptr<u4v>(a);
+    uint32_t acc = 0;
+    size_t i = begin + threadIdx.x;
+    for (; i + 3 * 512 < end; i += 4 * 512) {
+        const u4v v0 = __builtin_nontemporal_load(g + i), v1 = __builtin_nontemporal_load(g + i + 512);
+        const u4v v2 = __builtin_nontemporal_load(g + i + 1024), v3 = __builtin_nontemporal_load(g + i + 1536);
+        acc ^= (v0[0] ^ v0[1] ^ v0[2] ^ v0[3]) ^ (v1[0] ^ v1[1] ^ v1[2] ^ v1[3]) ^
+               (v2[0] ^ v2[1] ^ v2[2] ^ v2[3]) ^ (v3[0] ^ v3[1] ^ v3[2] ^ v3[3]);
+    }
+    for (; i < end; i += 512) {
+        const u4v v = __builtin_nontemporal_load(g + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m);
+    __shared__ uint32_t part[8];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) x ^= part[w];
+        *gptr_w<uint32_t>(sink + blockIdx.x) = x;
+    }
+}
+
 }  // namespace exq
 
 // =================================================================== host
@@ -532,6 +569,19 @@ exq_status exq_dequant(exq_layer_t L, void* w_out, void* stream) {
                        static_cast<uint16_t*>(w_out));
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? EXQ_OK : hip_fail(e, "dequant launch");
+}
+
+exq_status exq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int sink_words, void* stream) {
+    if (!buf || !sink) return fail(EXQ_ERR_INVALID_ARG, "NULL buffer");
+    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+        return fail(EXQ_ERR_INVALID_ARG, "buf must be 16-byte and sink 4-byte aligned");
+    if (bytes == 0 || bytes % 16) return fail(EXQ_ERR_INVALID_ARG, "bytes=%zu is not a positive multiple of 16", bytes);
+    if (sink_words < 1 || sink_words > (1 << 20)) return fail(EXQ_ERR_INVALID_ARG, "sink_words=%d not in [1, 2^20]", sink_words);
+    const size_t n16 = bytes / 16, chunk = (n16 + sink_words - 1) / sink_words;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(sink_words), dim3(512), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u4v*>(buf), n16, chunk, sink);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? EXQ_OK : hip_fail(e, "stream read launch");
 }
 
 exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* const* xs, const void* const* ys, int M,

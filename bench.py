@@ -120,6 +120,55 @@ def cpu_baseline(kept, M, gpu_ys, min_seconds):
     return secs, nbytes, worst, reps
 
 
+def gated_leg(exq, torch, layers, xs, M, nblk, steps, stream):
+    """The 80 gate/up pairs of the stack: h = SiLU(x Wg^T) * (x Wu^T) per block
+    as one exq_gemm_gated launch, against a two-linear plan plus torch's SiLU
+    and multiply (three launches and two fp16 intermediates)."""
+    from synth import BLOCK_SHAPES
+    names = [s[0] for s in BLOCK_SHAPES]
+    ig, iu = names.index("gate"), names.index("up")
+    pairs = [(layers[b * len(names) + ig], layers[b * len(names) + iu], xs[b * len(names) + ig]) for b in range(nblk)]
+    N = pairs[0][0].N
+    hs = [torch.empty((M, N), dtype=torch.float16, device="cuda") for _ in range(nblk)]
+    gs = [torch.empty((M, N), dtype=torch.float16, device="cuda") for _ in range(nblk)]
+    us = [torch.empty((M, N), dtype=torch.float16, device="cuda") for _ in range(nblk)]
+    plans = [exq.Plan([g, u], [x, x], [gs[b], us[b]], M) for b, (g, u, x) in enumerate(pairs)]
+
+    def fused():
+        for (g, u, x), h in zip(pairs, hs):
+            exq.exq_gemm_gated(x.data_ptr(), M, g.handle, u.handle, h.data_ptr(), stream)
+
+    def separate():
+        for b, p in enumerate(plans):
+            p.run(stream)
+            torch.mul(torch.nn.functional.silu(gs[b]), us[b], out=hs[b])
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_fused, ms_sep = timed(fused), timed(separate)
+    for p in plans:
+        p.close()
+    nbytes = 0
+    for g, u, x in pairs:
+        for l in (g, u):
+            nbytes += int(l.qweight.numel()) + int(l.scales.numel()) * 2 + 5 * (l.K // 128)
+        nbytes += 2 * M * g.K + 2 * M * N
+    log("gated gate/up: fused %.3f ms, plan + torch SiLU*mul %.3f ms per step" % (ms_fused, ms_sep))
+    return {"workload": "the %d gate/up pairs (8192 -> 28672, 2.55 bpw) of the stack, M=%d" % (nblk, M),
+            "ms_per_step_fused": round(ms_fused, 4), "GB/s_fused": round(nbytes / (ms_fused * 1e-3) / 1e9, 1),
+            "ms_per_step_plan_plus_torch_silu_mul": round(ms_sep, 4),
+            "bytes_per_step": nbytes}
+
+
 def prefill_leg(exq, torch, steps, warmup):
     """The seven 70B-shaped linears at M = 2048 (mixed 4.0 bpw) as one prefill
     plan launch per step; step time, the launch's own duration, and the same
@@ -209,6 +258,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--variants", action="store_true", help="also time per-linear calls, ungraphed and graphed")
     ap.add_argument("--no-stream-read", action="store_true", help="skip the plain streaming-read ceiling")
+    ap.add_argument("--no-gated", action="store_true", help="skip the fused gate/up (SiLU) leg")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="run a plain device copy of this size (for counter calibration) and exit")
     args = ap.parse_args()
@@ -347,6 +397,10 @@ def main():
         torch.cuda.empty_cache()
     log("graphed step %.3f ms; stream read %s" % (ms_step_graphed, read))
 
+    gated = None
+    if not args.no_gated and args.config == 5:
+        gated = gated_leg(exq, torch, layers, xs, M, nblk, args.steps, stream)
+
     traffic = None
     if os.path.exists(PROFILE_COUNTERS):
         with open(PROFILE_COUNTERS) as f:
@@ -449,6 +503,7 @@ def main():
         "ms_per_step_graphed": round(ms_step_graphed, 4),
         "step_stats": step_stats,
         "stream_read": read,
+        "gated_gate_up": gated,
         "cpu_baseline": cpu,
         "prefill": prefill,
     }

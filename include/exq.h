@@ -122,6 +122,28 @@ void exq_layer_destroy(exq_layer_t layer);
  * y_ref the exact (fp64) product of the fp16 inputs. */
 exq_status exq_gemm(const void* x, int M, exq_layer_t layer, void* y, void* stream);
 
+/* h = SiLU(x * Wg_hat^T) (.) (x * Wu_hat^T), SiLU(t) = t / (1 + e^-t): a gate
+ * and an up linear that share their input, fused with the activation between
+ * them.  (The exllamav3 article, section "technical deep dive", fuses
+ * matrix products and activation functions into single launches; SiLU of
+ * the gate product times the up product is the activation of the Llama
+ * feed-forward block, whose shapes the workloads use.)
+ *   x         device, fp16 [M][K] row-major, 16-byte aligned
+ *   gate, up  handles of equal K and N
+ *   h         device, fp16 [M][N] row-major, 16-byte aligned, must not overlap x
+ *   M >= 1.  M <= 16: one launch; a workgroup streams the same 64 (or 16)
+ *   columns of both linears and combines the two fp32 sums.  M > 16: the gate
+ *   product is written to h by the prefill kernel, and the up product's
+ *   epilogue reads it back (fp16) and writes SiLU(g) * u over it.
+ * Accuracy, with E_g, E_u the exq_gemm bounds of the two products and
+ * g_ref, u_ref their exact values:
+ *   |h - h_ref| <= 1.1 E_g (|u_ref| + E_u) + |SiLU(g_ref)| E_u
+ *                  + 2^-10 (|h_ref| + the terms before) + 1e-7
+ * (1.1 bounds |SiLU'|; 2^-10 covers the fp32 evaluation and the fp16 output
+ * rounding).  Deterministic.  Errors: INVALID_ARG (NULL, misaligned,
+ * overlapping, gate and up of different shapes), UNSUPPORTED, HIP. */
+exq_status exq_gemm_gated(const void* x, int M, exq_layer_t gate, exq_layer_t up, void* h, void* stream);
+
 /* Materialize W_hat^T: w_out device, fp16 [K][N] row-major (w_out[k*N + n]),
  * bit-exact fp16_RNE((c - 2^(b-1)) * s).  Meant for testing and inspection. */
 exq_status exq_dequant(exq_layer_t layer, void* w_out, void* stream);

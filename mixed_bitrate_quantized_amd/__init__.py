@@ -62,8 +62,9 @@ def _load():
     lib.exq_plan_destroy.argtypes = [vp]
     lib.exq_plan_destroy.restype = None
     lib.exq_stream_read.argtypes = [vp, u64, vp, i32, vp]
+    lib.exq_gemm_gated.argtypes = [vp, i32, vp, vp, vp, vp]
     for f in (lib.exq_pack, lib.exq_layer_create, lib.exq_gemm, lib.exq_dequant, lib.exq_plan_create,
-              lib.exq_plan_run, lib.exq_stream_read):
+              lib.exq_plan_run, lib.exq_stream_read, lib.exq_gemm_gated):
         f.restype = i32
     return lib
 
@@ -74,7 +75,7 @@ lib = _load()
 EXPORTED = (
     "exq_status_string", "exq_last_error", "exq_packed_bytes", "exq_pack", "exq_layer_create",
     "exq_layer_destroy", "exq_gemm", "exq_dequant", "exq_plan_create", "exq_plan_run", "exq_plan_destroy",
-    "exq_stream_read",
+    "exq_stream_read", "exq_gemm_gated",
 )
 
 
@@ -140,6 +141,10 @@ def exq_layer_destroy(handle: int) -> None:
 
 def exq_gemm(x_ptr: int, M: int, handle: int, y_ptr: int, stream=None) -> None:
     _check(lib.exq_gemm(x_ptr, M, handle, y_ptr, _stream_ptr(stream)), "exq_gemm")
+
+
+def exq_gemm_gated(x_ptr: int, M: int, gate: int, up: int, h_ptr: int, stream=None) -> None:
+    _check(lib.exq_gemm_gated(x_ptr, M, gate, up, h_ptr, _stream_ptr(stream)), "exq_gemm_gated")
 
 
 def exq_dequant(handle: int, w_ptr: int, stream=None) -> None:
@@ -217,6 +222,17 @@ class Layer:
             self.close()
         except Exception:
             pass
+
+
+def gemm_gated(x, gate: "Layer", up: "Layer", out=None, stream=None):
+    """x: torch fp16 [M][K] on the GPU -> h = SiLU(x gate^T) * (x up^T), fp16 [M][N]."""
+    import torch
+    assert x.dtype == torch.float16 and x.is_contiguous() and x.shape[-1] == gate.K
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, gate.N), dtype=torch.float16, device=x.device)
+    exq_gemm_gated(x.data_ptr(), M, gate.handle, up.handle, out.data_ptr(), stream)
+    return out
 
 
 class Plan:

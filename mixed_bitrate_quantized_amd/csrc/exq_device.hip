@@ -208,10 +208,12 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
     }
 }
 
-// One decode workgroup: TC columns, all of K, kWaves waves.  No prologue:
-// every wave starts streaming at once and only the final reduction is shared.
+// One decode tile: TC columns, all of K, kWaves waves.  No prologue: every
+// wave starts streaming at once and only the final reduction is shared.
+// decode_stream leaves each wave's partial sums in red (kWaves x M x TC
+// fp32); after a workgroup barrier the waves are added in order.
 template <int MB, int TC, bool M1>
-__device__ __forceinline__ void decode_wg(const LinearDev& L, int tile, int M, float* red) {
+__device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int M, float* red) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     DecodeCtx c;
@@ -252,13 +254,44 @@ __device__ __forceinline__ void decode_wg(const LinearDev& L, int tile, int M, f
             }
             if (4 * rb + r < M && lane < TC) red[(wave * M + 4 * rb + r) * TC + lane] = v;
         }
+}
+
+// Output (m, col) of a tile: the wave partials added in wave order.
+template <int TC>
+__device__ __forceinline__ float tile_sum(const float* red, int M, int m, int col) {
+    float v = red[(0 * M + m) * TC + col];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += red[(w * M + m) * TC + col];
+    return v;
+}
+
+template <int MB, int TC, bool M1>
+__device__ __forceinline__ void decode_wg(const LinearDev& L, int tile, int M, float* red) {
+    decode_stream<MB, TC, M1>(L, tile, M, red);
     __syncthreads();
     for (int t = threadIdx.x; t < M * TC; t += kWaves * 64) {
         const int m = t / TC, col = t % TC;
-        float v = red[(0 * M + m) * TC + col];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) v += red[(w * M + m) * TC + col];
-        *gptr_w<uint16_t>(L.y + (size_t)m * L.N + tile * TC + col) = f32_to_f16_bits(v);
+        *gptr_w<uint16_t>(L.y + (size_t)m * L.N + tile * TC + col) = f32_to_f16_bits(tile_sum<TC>(red, M, m, col));
+    }
+}
+
+// SiLU(g) * u in fp32: g / (1 + e^-g) * u.  For g far below zero e^-g
+// overflows to +inf and the product is a signed zero, the limit.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// A gate/up pair sharing x: every wave streams its share of the gate
+// linear's groups, then the same share of the up linear's, into two sets of
+// partials; the workgroup then writes h = SiLU(g) * u for its TC columns.
+template <int MB, int TC, bool M1>
+__global__ __launch_bounds__(kWaves * 64) void gated_decode_kernel(LinearDev G, LinearDev U, int M) {
+    __shared__ float red[2][kWaves * 4 * MB * TC];
+    decode_stream<MB, TC, M1>(G, blockIdx.x, M, red[0]);
+    decode_stream<MB, TC, M1>(U, blockIdx.x, M, red[1]);
+    __syncthreads();
+    for (int t = threadIdx.x; t < M * TC; t += kWaves * 64) {
+        const int m = t / TC, col = t % TC;
+        const float g = tile_sum<TC>(red[0], M, m, col), u = tile_sum<TC>(red[1], M, m, col);
+        *gptr_w<uint16_t>(G.y + (size_t)m * G.N + blockIdx.x * TC + col) = f32_to_f16_bits(silu_mul(g, u));
     }
 }
 
@@ -446,6 +479,24 @@ void launch_decode_mb(const LinearDev& d, int M, hipStream_t stream) {
     }
 }
 
+template <int MB, int TC, bool M1>
+void launch_gated_t(LinearDev g, LinearDev u, int M, hipStream_t stream) {
+    hipLaunchKernelGGL((gated_decode_kernel<MB, TC, M1>), dim3(g.N / TC), dim3(kWaves * 64), 0, stream, g, u, M);
+}
+
+template <int TC>
+void launch_gated_mb(const LinearDev& g, const LinearDev& u, int M, hipStream_t stream) {
+    switch ((M + 3) / 4) {
+        case 1:
+            if (M == 1) launch_gated_t<1, TC, true>(g, u, M, stream);
+            else launch_gated_t<1, TC, false>(g, u, M, stream);
+            break;
+        case 2: launch_gated_t<2, TC, false>(g, u, M, stream); break;
+        case 3: launch_gated_t<3, TC, false>(g, u, M, stream); break;
+        default: launch_gated_t<4, TC, false>(g, u, M, stream); break;
+    }
+}
+
 exq_status launch_decode(const LinearDev& d, int M, hipStream_t stream) {
     if (tile_cols_for(d.N) == 64) launch_decode_mb<64>(d, M, stream);
     else launch_decode_mb<16>(d, M, stream);
@@ -474,6 +525,7 @@ void launch_plan(const exq_plan* P, hipStream_t s) {
 }  // namespace
 
 extern exq_status exq_prefill_launch(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream);
+extern exq_status exq_prefill_launch_gated(const exq_layer* U, const void* x, int M, void* h, hipStream_t stream);
 extern int exq_prefill_tiles(const exq_layer* L, int M);
 extern exq_status exq_prefill_plan_launch(const LinearDev* d_list, const uint32_t* d_wg_map, int total_wgs, int M,
                                           hipStream_t stream);
@@ -558,6 +610,32 @@ exq_status exq_gemm(const void* x, int M, exq_layer_t L, void* y, void* stream) 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (M > kMaxDecodeM) return exq_prefill_launch(L, x, M, y, s);
     return exq_decode_rows(L, x, M, y, s);
+}
+
+exq_status exq_gemm_gated(const void* x, int M, exq_layer_t gate, exq_layer_t up, void* h, void* stream) {
+    if (!gate || !up) return fail(EXQ_ERR_INVALID_ARG, "layer is NULL");
+    if (!x || !h) return fail(EXQ_ERR_INVALID_ARG, "NULL x or h");
+    if (M < 1) return fail(EXQ_ERR_INVALID_ARG, "M=%d must be >= 1", M);
+    if (gate->K != up->K || gate->N != up->N)
+        return fail(EXQ_ERR_INVALID_ARG, "gate (K=%d, N=%d) and up (K=%d, N=%d) differ in shape", gate->K, gate->N,
+                    up->K, up->N);
+    if (!aligned16(x) || !aligned16(h)) return fail(EXQ_ERR_INVALID_ARG, "x and h must be 16-byte aligned");
+    if (overlap(x, 2 * (size_t)M * gate->K, h, 2 * (size_t)M * gate->N))
+        return fail(EXQ_ERR_INVALID_ARG, "h overlaps x");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M > kMaxDecodeM) {
+        // Gate product into h, then the up product's epilogue combines in place.
+        exq_status st = exq_prefill_launch(gate, x, M, h, s);
+        return st != EXQ_OK ? st : exq_prefill_launch_gated(up, x, M, h, s);
+    }
+    // The tile width follows exq_gemm's rule.  (16-column tiles for the
+    // 28672-column feed-forward pair, which fills only 448 of the 512 slots
+    // with 64-column tiles, measured twice as slow.)
+    const LinearDev g = linear_dev(gate, x, h), u = linear_dev(up, x, nullptr);
+    if (tile_cols_for(gate->N) == 64) launch_gated_mb<64>(g, u, M, s);
+    else launch_gated_mb<16>(g, u, M, s);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? EXQ_OK : hip_fail(e, "gated decode launch");
 }
 
 exq_status exq_dequant(exq_layer_t L, void* w_out, void* stream) {

@@ -279,7 +279,16 @@ __device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx&
     T_n = kDq[src1.b];
 }
 
-// One 256 x 256 output tile (rows m0.., columns n0..) over all of K.
+// SiLU(g) * u in fp32 (g read back as fp16): g / (1 + e^-g) * u.
+__device__ __forceinline__ float silu_mul_h(uint16_t g16, float u) {
+    const float g = (float)__builtin_bit_cast(_Float16, g16);
+    return g / (1.0f + expf(-g)) * u;
+}
+
+// One 256 x 256 output tile (rows m0.., columns n0..) over all of K.  GATED:
+// y already holds the gate product g (fp16) of the same tile, and the tile
+// stores SiLU(g) * acc over it.
+template <bool GATED>
 __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, int n0, uint16_t* sx0,
                                              uint16_t* sx1) {
     PrefillCtx c;
@@ -355,16 +364,24 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
             for (int a = 0; a < 4; ++a) {
                 const int n = n0 + 64 * c.wave + 32 * ib + 8 * a + 4 * lh;
                 if (n >= L.N) continue;
-                const uint32_t lo = (uint32_t)f32_to_f16_bits(acc[ib][jb][4 * a]) |
-                                    ((uint32_t)f32_to_f16_bits(acc[ib][jb][4 * a + 1]) << 16);
-                const uint32_t hi = (uint32_t)f32_to_f16_bits(acc[ib][jb][4 * a + 2]) |
-                                    ((uint32_t)f32_to_f16_bits(acc[ib][jb][4 * a + 3]) << 16);
+                float o[4] = {acc[ib][jb][4 * a], acc[ib][jb][4 * a + 1], acc[ib][jb][4 * a + 2],
+                              acc[ib][jb][4 * a + 3]};
+                if constexpr (GATED) {
+                    const u2v g = *gptr_w<u2v>(L.y + (size_t)m * L.N + n);
+                    o[0] = silu_mul_h((uint16_t)(g[0] & 0xFFFFu), o[0]);
+                    o[1] = silu_mul_h((uint16_t)(g[0] >> 16), o[1]);
+                    o[2] = silu_mul_h((uint16_t)(g[1] & 0xFFFFu), o[2]);
+                    o[3] = silu_mul_h((uint16_t)(g[1] >> 16), o[3]);
+                }
+                const uint32_t lo = (uint32_t)f32_to_f16_bits(o[0]) | ((uint32_t)f32_to_f16_bits(o[1]) << 16);
+                const uint32_t hi = (uint32_t)f32_to_f16_bits(o[2]) | ((uint32_t)f32_to_f16_bits(o[3]) << 16);
                 const u2v v = {lo, hi};
                 *gptr_w<u2v>(L.y + (size_t)m * L.N + n) = v;
             }
     }
 }
 
+template <bool GATED>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, int row_tiles, int col_tiles) {
     __shared__ __attribute__((aligned(16))) uint16_t sx0[kPT * kPLd];
     __shared__ __attribute__((aligned(16))) uint16_t sx1[kPT * kPLd];
@@ -372,7 +389,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, 
     const int T = row_tiles * col_tiles;
     const int i = blockIdx.x, xcd = i & 7, per = T >> 3, rem = T & 7;
     const int t = xcd * per + min(xcd, rem) + (i >> 3);
-    prefill_tile(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sx0, sx1);
+    prefill_tile<GATED>(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sx0, sx1);
 }
 
 // Several linears in one launch: workgroup i takes entry i of wg_map
@@ -394,7 +411,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_plan_kernel(const LinearDev
             dst[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)src[k]);   // uniform: SGPRs
     }
     const int col_tiles = (L.N + kPT - 1) / kPT, t = (int)(e >> 16);
-    prefill_tile(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sx0, sx1);
+    prefill_tile<false>(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sx0, sx1);
 }
 
 }  // namespace
@@ -402,17 +419,31 @@ __global__ __launch_bounds__(kPThreads) void prefill_plan_kernel(const LinearDev
 
 using namespace exq;
 
-exq_status exq_prefill_launch(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream) {
+namespace {
+
+template <bool GATED>
+exq_status prefill_launch(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream) {
     // Offsets into one tile's rows of x are 32-bit: 2 * 256 * K bytes must stay below 2^31.
     if ((size_t)2 * kPT * (size_t)L->K >= (size_t)kBufOOB)
         return fail(EXQ_ERR_UNSUPPORTED, "K=%d is too large for the prefill kernel", L->K);
     const long row_tiles = (M + kPT - 1) / kPT, col_tiles = (L->N + kPT - 1) / kPT;
     if (row_tiles * col_tiles > INT_MAX) return fail(EXQ_ERR_UNSUPPORTED, "M=%d gives too many tiles", M);
     LinearDev d = linear_dev(L, x, y);
-    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)(row_tiles * col_tiles)), dim3(kPThreads), 0, stream, d, M,
-                       (int)row_tiles, (int)col_tiles);
+    hipLaunchKernelGGL(prefill_kernel<GATED>, dim3((unsigned)(row_tiles * col_tiles)), dim3(kPThreads), 0, stream, d,
+                       M, (int)row_tiles, (int)col_tiles);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? EXQ_OK : fail(EXQ_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+exq_status exq_prefill_launch(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream) {
+    return prefill_launch<false>(L, x, M, y, stream);
+}
+
+// h holds the gate product; writes SiLU(h) * (x W_up^T) over it.
+exq_status exq_prefill_launch_gated(const exq_layer* U, const void* x, int M, void* h, hipStream_t stream) {
+    return prefill_launch<true>(U, x, M, h, stream);
 }
 
 // Tiles of one linear in a prefill plan (0 if the linear cannot be planned).

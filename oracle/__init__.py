@@ -174,6 +174,48 @@ def gemm_packed_cols(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray, wid
     return y, bnd
 
 
+# Bound on |SiLU'(t)| over all t: SiLU'(t) = s(t) (1 + t (1 - s(t))) with s the
+# logistic function peaks at 1.0998 (t = 2.3994) and bottoms at -0.0998.
+SILU_SLOPE_BOUND = 1.1
+
+
+def silu(t):
+    """SiLU(t) = t / (1 + e^-t) in float64, elementwise (e^-t overflowing to inf gives the signed-zero limit)."""
+    t = np.asarray(t, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return t / (1.0 + np.exp(-t))
+
+
+def gated(x: np.ndarray, w_gate_hat: np.ndarray, w_up_hat: np.ndarray, rel: float = 2e-3, abs_: float = 1e-5):
+    """(h_ref, allowance) float64 [M][N] for h = SiLU(x Wg_hat^T) * (x Wu_hat^T).
+
+    h_ref uses the exact (fp64) products g, u of the fp16 inputs.  A result
+    whose two products each meet the matmul tolerance (E = rel * sum|x w| +
+    abs_) and that evaluates SiLU(g) * u in fp32 and rounds it to fp16 is
+    within
+        1.1 E_g (|u| + E_u) + |SiLU(g)| E_u + 2^-10 (|h| + those terms) + 1e-7
+    of h_ref: the first two terms bound |SiLU(g') u' - SiLU(g) u| for
+    |g' - g| <= E_g, |u' - u| <= E_u by the mean value theorem, the third
+    the fp32 evaluation and the fp16 rounding (relative 2^-11), the last the
+    fp16 subnormal spacing."""
+    g, bg = gemm(x, w_gate_hat)
+    u, bu = gemm(x, w_up_hat)
+    eg, eu = rel * bg + abs_, rel * bu + abs_
+    s = silu(g)
+    h = s * u
+    terms = SILU_SLOPE_BOUND * eg * (np.abs(u) + eu) + np.abs(s) * eu
+    return h, terms + 2.0 ** -10 * (np.abs(h) + terms) + 1e-7
+
+
+def within_allowance(y: np.ndarray, y_ref: np.ndarray, allowance: np.ndarray):
+    """(ok, worst ratio of error to allowance) for a per-output allowance."""
+    y = np.asarray(y, dtype=np.float64)
+    err = np.abs(y - y_ref)
+    ratio = err / allowance
+    worst = float(np.max(ratio)) if ratio.size else 0.0
+    return bool(np.all(err <= allowance) and np.all(np.isfinite(y))), worst
+
+
 def reference_layer(W: np.ndarray, widths):
     """Oracle's own quantize + pack of a layer: (codes, scales, qweight)."""
     codes, scales = quantize(W, widths)

@@ -120,6 +120,83 @@ def cpu_baseline(kept, M, gpu_ys, min_seconds):
     return secs, nbytes, worst, reps
 
 
+def lp_lower_bound(err, size, budget, lo_opt):
+    """Optimum of the linear relaxation of the multiple-choice knapsack (a
+    lower bound on any allocation's error): each group's options above its
+    minimum reduced to the lower convex hull of (bits, error), hull segments
+    taken in order of error saved per bit, the last one fractionally."""
+    WID = np.array([2, 3, 4, 5, 6, 8], dtype=np.float64)
+    total = 0.0
+    segs = []
+    spent = 0.0
+    for g in range(err.shape[0]):
+        j0 = int(lo_opt[g])
+        total += err[g, j0]
+        spent += WID[j0] * size[g]
+        hull = [j0]
+        for j in range(j0 + 1, 6):
+            if err[g, j] >= err[g, hull[-1]]:
+                continue
+            while len(hull) >= 2:
+                a, b = hull[-2], hull[-1]
+                if (err[g, a] - err[g, j]) / (WID[j] - WID[a]) >= (err[g, a] - err[g, b]) / (WID[b] - WID[a]):
+                    hull.pop()
+                else:
+                    break
+            hull.append(j)
+        for a, b in zip(hull, hull[1:]):
+            cost = (WID[b] - WID[a]) * size[g]
+            segs.append(((err[g, a] - err[g, b]) / cost, cost, err[g, a] - err[g, b]))
+    left = budget - spent
+    for rate, cost, gain in sorted(segs, key=lambda s: -s[0]):
+        if left <= 0:
+            break
+        take = min(1.0, left / cost)
+        total -= take * gain
+        left -= take * cost
+    return total
+
+
+def allocator_leg(exq, kept, nblk):
+    """Host-side bit allocation (the offline step): measure block 0's seven
+    linears (squared weight error at every width, exq_group_errors), then
+    allocate widths over the whole stack at the seeded schedule's bit budget
+    with the schedule's >= 6-bit groups kept (exq_allocate_widths; block 0's
+    tables stand for every block)."""
+    from synth import workloads
+    if not kept:
+        specs = workloads.linears(3)
+        kept = []
+        for spec in specs:
+            W = workloads.make_weight(spec)
+            kept.append((spec, W, workloads.make_widths(spec, W)))
+    t0 = time.perf_counter()
+    tables = [exq.exq_group_errors(W) for _, W, _ in kept]
+    t_measure = time.perf_counter() - t0
+    WID = np.array([2, 3, 4, 5, 6, 8])
+    err = np.concatenate(tables * nblk)
+    size = np.concatenate([np.full(t.shape[0], spec.N // 1024, dtype=np.int32) for (spec, _, _), t in zip(kept, tables)] * nblk)
+    sched = np.concatenate([np.asarray(w, dtype=np.int64) for _, _, w in kept] * nblk)
+    forced = np.where(sched >= 6, 6, 0).astype(np.uint8)
+    budget = int((sched * size).sum())
+    iters = 20 * err.shape[0]
+    t0 = time.perf_counter()
+    widths, total = exq.exq_allocate_widths(err, size, budget, forced, seed=1, iterations=iters)
+    t_alloc = time.perf_counter() - t0
+    sched_err = float(err[np.arange(err.shape[0]), np.searchsorted(WID, sched)].sum())
+    bound = lp_lower_bound(err, size, budget, np.where(forced >= 6, 4, 0))
+    bits = int((widths.astype(np.int64) * size).sum())
+    log("allocator: measure %.2f s, allocate %d groups %.2f s, error %.4g vs schedule %.4g" % (
+        t_measure, err.shape[0], t_alloc, total, sched_err))
+    return {"measure_s_block0": round(t_measure, 3), "allocate_s_stack": round(t_alloc, 3), "groups": int(err.shape[0]),
+            "iterations": iters, "cores": omp_threads(),
+            "bpw_allocated": round(bits / float(size.sum()), 4),
+            "error_vs_seeded_schedule": round(total / sched_err, 4),
+            "error_vs_lp_lower_bound": round(total / bound, 6),
+            "workload": "squared weight error of block 0's 7 linears at 2..8 bits; widths for the %d-block stack at "
+                        "the seeded schedule's budget (2.55 bpw per linear), its >= 6-bit groups kept" % nblk}
+
+
 def gated_leg(exq, torch, layers, xs, M, nblk, steps, stream):
     """The 80 gate/up pairs of the stack: h = SiLU(x Wg^T) * (x Wu^T) per block
     as one exq_gemm_gated launch, against a two-linear plan plus torch's SiLU
@@ -259,6 +336,7 @@ def main():
     ap.add_argument("--variants", action="store_true", help="also time per-linear calls, ungraphed and graphed")
     ap.add_argument("--no-stream-read", action="store_true", help="skip the plain streaming-read ceiling")
     ap.add_argument("--no-gated", action="store_true", help="skip the fused gate/up (SiLU) leg")
+    ap.add_argument("--no-allocator", action="store_true", help="skip the host bit-allocation leg")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="run a plain device copy of this size (for counter calibration) and exit")
     args = ap.parse_args()
@@ -457,6 +535,10 @@ def main():
                           cbytes / 1e9, worst),
         }
 
+    alloc = None
+    if not args.no_allocator and args.config == 5:
+        alloc = allocator_leg(exq, kept if len(kept) == len(BLOCK_SHAPES) else None, nblk)
+
     prefill = None
     if not args.no_prefill:
         for p in plans:
@@ -504,6 +586,7 @@ def main():
         "step_stats": step_stats,
         "stream_read": read,
         "gated_gate_up": gated,
+        "allocator": alloc,
         "cpu_baseline": cpu,
         "prefill": prefill,
     }

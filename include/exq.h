@@ -92,6 +92,46 @@ size_t exq_packed_bytes(int K, int N, int group_size, const uint8_t* widths);
 exq_status exq_pack(const float* W, int K, int N, int group_size, const uint8_t* widths,
                     void* qweight_out, uint16_t* scales_out);
 
+/* ------------------------------------------------- bit-width allocation */
+
+/* The offline measurement and optimizer of the exllamav2 report (sections
+ * 创新之处 and 关键设计决策: every candidate setting is measured once and a
+ * simulated-annealing solver picks one per block to meet the bit budget).
+ * Here a block is a group of 128 input channels of one linear, the
+ * candidates are the widths {2,3,4,5,6,8}, and the measured error is the
+ * squared weight error of this library's own quantizer (no calibration data:
+ * see the design notes).
+ *
+ * exq_group_errors: err_out[g*6 + j] = sum over the group's N x 128 weights of
+ * (w - w_hat)^2 at width {2,3,4,5,6,8}[j], w_hat = fp16_RNE((c - z) s) exactly as
+ * exq_pack / exq_dequant produce it; accumulated in double, column order.
+ *   W        host fp32 [N][K]; err_out host double [K/128][6]
+ * Errors: INVALID_ARG (NULL, bad shape, non-finite W, a scale overflowing
+ * fp16), UNSUPPORTED (group_size != 128). */
+exq_status exq_group_errors(const float* W, int K, int N, int group_size, double* err_out);
+
+/* exq_allocate_widths: choose width b_g in {2,3,4,5,6,8} for each of G groups,
+ * b_g >= min_width[g], minimizing sum_g err[g][b_g] subject to
+ * sum_g b_g * size[g] <= budget.  size[g] is the group's column count (its
+ * bits are b_g * 128 * size[g]), so groups of several linears can share one
+ * budget.  Start: the greedy of the multiple-choice knapsack on each group's
+ * lower convex hull; then `iterations` simulated-annealing moves (change one
+ * group; if that breaks the budget, pay for it by lowering other groups one
+ * step at a time, each the cheapest per bit freed of four random ones;
+ * Metropolis acceptance, geometric cooling over six decades) with a
+ * SplitMix64 stream seeded by `seed`, then any budget left is spent
+ * greedily.  The best state seen is kept, so the result never has more error
+ * than the greedy start.  Deterministic for given inputs.
+ *   err        host double [G][6], each >= 0 and finite
+ *   size       host int32 [G], each >= 1
+ *   min_width  host uint8 [G] or NULL (0 = no bound)
+ *   widths_out host uint8 [G]; total_err_out host double or NULL
+ * Errors: INVALID_ARG (NULL, G < 1, bad entries, iterations < 0, or a budget
+ * below the smallest allowed cost). */
+exq_status exq_allocate_widths(const double* err, const int32_t* size, int G, int64_t budget,
+                               const uint8_t* min_width, uint64_t seed, int64_t iterations, uint8_t* widths_out,
+                               double* total_err_out);
+
 /* --------------------------------------------------------- device layers */
 
 /* Describe a packed layer already resident in device memory.

@@ -63,8 +63,11 @@ def _load():
     lib.exq_plan_destroy.restype = None
     lib.exq_stream_read.argtypes = [vp, u64, vp, i32, vp]
     lib.exq_gemm_gated.argtypes = [vp, i32, vp, vp, vp, vp]
+    lib.exq_group_errors.argtypes = [vp, i32, i32, i32, vp]
+    lib.exq_allocate_widths.argtypes = [vp, vp, i32, ctypes.c_int64, vp, ctypes.c_uint64, ctypes.c_int64, vp, vp]
     for f in (lib.exq_pack, lib.exq_layer_create, lib.exq_gemm, lib.exq_dequant, lib.exq_plan_create,
-              lib.exq_plan_run, lib.exq_stream_read, lib.exq_gemm_gated):
+              lib.exq_plan_run, lib.exq_stream_read, lib.exq_gemm_gated, lib.exq_group_errors,
+              lib.exq_allocate_widths):
         f.restype = i32
     return lib
 
@@ -75,7 +78,7 @@ lib = _load()
 EXPORTED = (
     "exq_status_string", "exq_last_error", "exq_packed_bytes", "exq_pack", "exq_layer_create",
     "exq_layer_destroy", "exq_gemm", "exq_dequant", "exq_plan_create", "exq_plan_run", "exq_plan_destroy",
-    "exq_stream_read", "exq_gemm_gated",
+    "exq_stream_read", "exq_gemm_gated", "exq_group_errors", "exq_allocate_widths",
 )
 
 
@@ -145,6 +148,29 @@ def exq_gemm(x_ptr: int, M: int, handle: int, y_ptr: int, stream=None) -> None:
 
 def exq_gemm_gated(x_ptr: int, M: int, gate: int, up: int, h_ptr: int, stream=None) -> None:
     _check(lib.exq_gemm_gated(x_ptr, M, gate, up, h_ptr, _stream_ptr(stream)), "exq_gemm_gated")
+
+
+def exq_group_errors(W: np.ndarray) -> np.ndarray:
+    """Squared weight error of every group at every width: float64 [K/128][6] from W fp32 [N][K]."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    err = np.empty((K // 128, 6), dtype=np.float64)
+    _check(lib.exq_group_errors(_np_ptr(W), K, N, 128, _np_ptr(err)), "exq_group_errors")
+    return err
+
+
+def exq_allocate_widths(err: np.ndarray, size, budget: int, min_width=None, seed: int = 0, iterations: int = 0):
+    """(widths uint8 [G], total error) minimizing sum err[g][b_g] with sum b_g * size[g] <= budget."""
+    err = np.ascontiguousarray(err, dtype=np.float64)
+    G = err.shape[0]
+    size = np.ascontiguousarray(np.broadcast_to(np.asarray(size, dtype=np.int32), (G,)))
+    mw = None if min_width is None else np.ascontiguousarray(min_width, dtype=np.uint8)
+    out = np.empty(G, dtype=np.uint8)
+    total = ctypes.c_double()
+    _check(lib.exq_allocate_widths(_np_ptr(err), _np_ptr(size), G, int(budget), None if mw is None else _np_ptr(mw),
+                                   int(seed) & ((1 << 64) - 1), int(iterations), _np_ptr(out), ctypes.byref(total)),
+           "exq_allocate_widths")
+    return out, total.value
 
 
 def exq_dequant(handle: int, w_ptr: int, stream=None) -> None:

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <vector>
 
 #include "exq_internal.h"
 
@@ -143,6 +144,42 @@ WavePlan plan_waves(int K, const uint8_t* widths) {
     return p;
 }
 
+// ------------------------------------------------------- width allocation
+
+constexpr int kNumOpts = 6;
+constexpr int kOptWidth[kNumOpts] = {2, 3, 4, 5, 6, 8};
+
+// Squared error sum_i (w_i - w_hat_i)^2 of one column's group at width b,
+// with the packer's quantizer and the exact dequantization rounding.
+static double column_group_error(const float* w, int b) {
+    const int qmax = (1 << (b - 1)) - 1;
+    float amax = 0.0f;
+    for (int i = 0; i < kGroup; ++i) amax = std::max(amax, std::fabs(w[i]));
+    const float s = f16_to_f32(f32_to_f16(amax / (float)qmax));
+    double e = 0.0;
+    for (int i = 0; i < kGroup; ++i) {
+        float q = 0.0f;
+        if (s != 0.0f) q = std::min(std::max(std::nearbyint(w[i] / s), (float)-qmax), (float)qmax);
+        const double d = (double)w[i] - (double)f16_to_f32(f32_to_f16(q * s));   // q * s is exact in fp32
+        e += d * d;
+    }
+    return e;
+}
+
+// SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): a 64-bit counter passed
+// through a fixed mixing function; one draw per call.
+struct SplitMix64 {
+    uint64_t x;
+    uint64_t next() {
+        uint64_t z = (x += 0x9E3779B97F4A7C15ull);
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        return z ^ (z >> 31);
+    }
+    double uniform() { return (double)(next() >> 11) * 0x1.0p-53; }   // [0, 1)
+    uint32_t below(uint32_t n) { return (uint32_t)(((next() >> 32) * (uint64_t)n) >> 32); }
+};
+
 }  // namespace exq
 
 using namespace exq;
@@ -213,6 +250,214 @@ exq_status exq_pack(const float* W, int K, int N, int group_size, const uint8_t*
     }
     if (bad & 1) return fail(EXQ_ERR_INVALID_ARG, "W holds a NaN or infinity");
     if (bad & 2) return fail(EXQ_ERR_INVALID_ARG, "a group scale overflows fp16 (|w| too large)");
+    return EXQ_OK;
+}
+
+exq_status exq_group_errors(const float* W, int K, int N, int group_size, double* err_out) {
+    if (!W || !err_out) return fail(EXQ_ERR_INVALID_ARG, "NULL buffer");
+    if (K <= 0 || N <= 0 || K % kGroup) return fail(EXQ_ERR_INVALID_ARG, "bad shape K=%d N=%d", K, N);
+    if (group_size != kGroup) return fail(EXQ_ERR_UNSUPPORTED, "group_size=%d (only 128)", group_size);
+    const int G = K / kGroup;
+    int bad = 0;
+    // One group per task, columns in order: the sums do not depend on the thread count.
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int g = 0; g < G; ++g) {
+        double acc[kNumOpts] = {0, 0, 0, 0, 0, 0};
+        for (int n = 0; n < N; ++n) {
+            const float* w = W + (size_t)n * K + (size_t)g * kGroup;
+            float amax = 0.0f;
+            for (int i = 0; i < kGroup; ++i) {
+                const float a = std::fabs(w[i]);
+                if (!(a <= 3.4e38f)) bad |= 1;
+                amax = std::max(amax, a);
+            }
+            if (amax / 1.0f > 65504.0f) bad |= 2;   // the 2-bit scale max|w| / 1 must stay finite in fp16
+            if (bad) continue;
+            for (int j = 0; j < kNumOpts; ++j) acc[j] += column_group_error(w, kOptWidth[j]);
+        }
+        for (int j = 0; j < kNumOpts; ++j) err_out[(size_t)g * kNumOpts + j] = acc[j];
+    }
+    if (bad & 1) return fail(EXQ_ERR_INVALID_ARG, "W holds a NaN or infinity");
+    if (bad & 2) return fail(EXQ_ERR_INVALID_ARG, "a group scale overflows fp16 (|w| too large)");
+    return EXQ_OK;
+}
+
+exq_status exq_allocate_widths(const double* err, const int32_t* size, int G, int64_t budget,
+                               const uint8_t* min_width, uint64_t seed, int64_t iterations, uint8_t* widths_out,
+                               double* total_err_out) {
+    if (!err || !size || !widths_out) return fail(EXQ_ERR_INVALID_ARG, "NULL buffer");
+    if (G < 1) return fail(EXQ_ERR_INVALID_ARG, "G=%d must be >= 1", G);
+    if (iterations < 0) return fail(EXQ_ERR_INVALID_ARG, "iterations must be >= 0");
+    // Allowed options of each group: lo[g] .. 5 (widths at or above min_width).
+    std::vector<int> lo(G), cur(G);
+    int64_t cost = 0;
+    for (int g = 0; g < G; ++g) {
+        if (size[g] < 1) return fail(EXQ_ERR_INVALID_ARG, "size[%d]=%d must be >= 1", g, size[g]);
+        for (int j = 0; j < kNumOpts; ++j)
+            if (!(err[(size_t)g * kNumOpts + j] >= 0.0) || !std::isfinite(err[(size_t)g * kNumOpts + j]))
+                return fail(EXQ_ERR_INVALID_ARG, "err[%d][%d] is negative or not finite", g, j);
+        const int mw = min_width ? min_width[g] : 0;
+        if (mw > 8) return fail(EXQ_ERR_INVALID_ARG, "min_width[%d]=%d above 8", g, mw);
+        lo[g] = 0;
+        while (kOptWidth[lo[g]] < mw) ++lo[g];
+        cur[g] = lo[g];
+        cost += (int64_t)kOptWidth[lo[g]] * size[g];
+    }
+    if (cost > budget)
+        return fail(EXQ_ERR_INVALID_ARG, "budget %lld is below the smallest allowed cost %lld", (long long)budget,
+                    (long long)cost);
+    auto E = [&](int g, int j) { return err[(size_t)g * kNumOpts + j]; };
+    auto C = [&](int g, int j) { return (int64_t)kOptWidth[j] * size[g]; };
+
+    // Start: the greedy of the multiple-choice knapsack.  Each group's
+    // options are reduced to the lower convex hull of (cost, error) above
+    // its minimum; hull steps are taken in order of error saved per bit as
+    // long as they fit.
+    {
+        struct Step { double gain; int g, from, to; };
+        std::vector<std::vector<int>> hull(G);
+        for (int g = 0; g < G; ++g) {
+            std::vector<int>& h = hull[g];
+            h.push_back(lo[g]);
+            for (int j = lo[g] + 1; j < kNumOpts; ++j) {
+                if (E(g, j) >= E(g, h.back())) continue;   // dominated: costs more, saves nothing
+                while (h.size() >= 2) {
+                    const int a = h[h.size() - 2], b = h.back();
+                    // b is not on the lower hull if the slope a->j is at least as steep as a->b
+                    const double sab = (E(g, a) - E(g, b)) / (double)(C(g, b) - C(g, a));
+                    const double saj = (E(g, a) - E(g, j)) / (double)(C(g, j) - C(g, a));
+                    if (saj >= sab) h.pop_back();
+                    else break;
+                }
+                h.push_back(j);
+            }
+        }
+        auto cmp = [](const Step& x, const Step& y) { return x.gain < y.gain || (x.gain == y.gain && x.g > y.g); };
+        std::vector<Step> heap;
+        std::vector<size_t> pos(G, 0);
+        auto push_next = [&](int g) {
+            if (pos[g] + 1 < hull[g].size()) {
+                const int a = hull[g][pos[g]], b = hull[g][pos[g] + 1];
+                heap.push_back({(E(g, a) - E(g, b)) / (double)(C(g, b) - C(g, a)), g, a, b});
+                std::push_heap(heap.begin(), heap.end(), cmp);
+            }
+        };
+        for (int g = 0; g < G; ++g) push_next(g);
+        while (!heap.empty()) {
+            std::pop_heap(heap.begin(), heap.end(), cmp);
+            const Step s = heap.back();
+            heap.pop_back();
+            const int64_t dc = C(s.g, s.to) - C(s.g, s.from);
+            if (cost + dc > budget) continue;   // this group stops here
+            cost += dc;
+            cur[s.g] = s.to;
+            ++pos[s.g];
+            push_next(s.g);
+        }
+    }
+
+    // Simulated annealing from the greedy start.  A move sets one group to
+    // another allowed width.  If that breaks the budget, it is paid for by
+    // lowering other groups one allowed step at a time, each time the one
+    // that adds the least error per bit freed among four random candidates,
+    // until the move fits (at most 64 steps): one wide group can so be paid
+    // for by many narrow ones.  The whole move is accepted by the Metropolis
+    // rule at a temperature falling geometrically over six decades from a
+    // tenth of the mean size of single-step changes at the start; the best
+    // state seen, topped up greedily with any budget it leaves, is returned.
+    double total = 0.0;
+    for (int g = 0; g < G; ++g) total += E(g, cur[g]);
+    std::vector<int> best = cur;
+    double best_total = total;
+    SplitMix64 rng{seed};
+    if (iterations > 0) {
+        double t0 = 0.0;
+        int samples = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int g = (int)rng.below((uint32_t)G), j = cur[g];
+            const int k = (j + 1 < kNumOpts) ? j + 1 : j - 1;
+            if (k < lo[g] || k < 0) continue;
+            t0 += std::fabs(E(g, k) - E(g, j));
+            ++samples;
+        }
+        t0 = samples ? t0 / samples : 1.0;
+        if (!(t0 > 0.0)) t0 = 1.0;
+        const double cool = std::pow(1e-6, 1.0 / (double)iterations);
+        double T = 0.1 * t0;
+        std::vector<std::pair<int, int>> undo;   // (group, previous option) of the groups a move lowered
+        for (int64_t it = 0; it < iterations; ++it, T *= cool) {
+            const int g = (int)rng.below((uint32_t)G);
+            const int span = kNumOpts - lo[g];
+            if (span < 2) continue;
+            int j = lo[g] + (int)rng.below((uint32_t)(span - 1));
+            if (j >= cur[g]) ++j;   // any allowed option but the current one
+            const int jg = cur[g];
+            int64_t dc = C(g, j) - C(g, jg);
+            double de = E(g, j) - E(g, jg);
+            cur[g] = j;
+            undo.clear();
+            bool fits = cost + dc <= budget;
+            for (int step = 0; !fits && step < 64; ++step) {
+                int h = -1;
+                double rate = 0.0;
+                for (int t = 0; t < 4; ++t) {
+                    const int c = (int)rng.below((uint32_t)G);
+                    if (c == g || cur[c] == lo[c]) continue;
+                    const double r = (E(c, cur[c] - 1) - E(c, cur[c])) / (double)(C(c, cur[c]) - C(c, cur[c] - 1));
+                    if (h < 0 || r < rate) {
+                        h = c;
+                        rate = r;
+                    }
+                }
+                if (h < 0) continue;
+                undo.push_back({h, cur[h]});
+                dc += C(h, cur[h] - 1) - C(h, cur[h]);
+                de += E(h, cur[h] - 1) - E(h, cur[h]);
+                --cur[h];
+                fits = cost + dc <= budget;
+            }
+            if (fits && (de <= 0.0 || rng.uniform() < std::exp(-de / T))) {
+                cost += dc;
+                total += de;
+                if (total < best_total) {
+                    best_total = total;
+                    best = cur;
+                }
+            } else {
+                for (size_t u = undo.size(); u-- > 0;) cur[undo[u].first] = undo[u].second;
+                cur[g] = jg;
+            }
+        }
+    }
+    // Polish: spend any budget left over on the single-group upgrades that
+    // save the most error per bit.
+    {
+        cost = 0;
+        for (int g = 0; g < G; ++g) cost += C(g, best[g]);
+        for (;;) {
+            int bg = -1, bj = -1;
+            double bgain = 0.0;
+            for (int g = 0; g < G; ++g)
+                for (int j = best[g] + 1; j < kNumOpts; ++j) {
+                    const int64_t dc = C(g, j) - C(g, best[g]);
+                    const double gain = (E(g, best[g]) - E(g, j)) / (double)dc;
+                    if (cost + dc <= budget && gain > bgain) {
+                        bgain = gain;
+                        bg = g;
+                        bj = j;
+                    }
+                }
+            if (bg < 0) break;
+            cost += C(bg, bj) - C(bg, best[bg]);
+            best[bg] = bj;
+        }
+    }
+    double sum = 0.0;   // recomputed in group order, free of the running sum's drift
+    for (int g = 0; g < G; ++g) {
+        widths_out[g] = (uint8_t)kOptWidth[best[g]];
+        sum += E(g, best[g]);
+    }
+    if (total_err_out) *total_err_out = sum;
     return EXQ_OK;
 }
 

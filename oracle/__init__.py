@@ -216,6 +216,61 @@ def within_allowance(y: np.ndarray, y_ref: np.ndarray, allowance: np.ndarray):
     return bool(np.all(err <= allowance) and np.all(np.isfinite(y))), worst
 
 
+ALLOC_WIDTHS = (2, 3, 4, 5, 6, 8)
+
+
+def group_errors(W: np.ndarray) -> np.ndarray:
+    """float64 [G][6]: sum over each group's N x 128 weights of (w - w_hat)^2 at each
+    width, w_hat from this oracle's own quantize and dequant."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    G = K // GROUP
+    err = np.empty((G, len(ALLOC_WIDTHS)), dtype=np.float64)
+    for j, b in enumerate(ALLOC_WIDTHS):
+        widths = [b] * G
+        codes, scales = quantize(W, widths)
+        w_hat = dequant(codes, scales, widths).view(np.float16).astype(np.float64)   # [K][N]
+        d = W.astype(np.float64).T - w_hat
+        err[:, j] = (d * d).reshape(G, GROUP, N).sum(axis=(1, 2))
+    return err
+
+
+def allocate_exact(err, size, budget: int, min_width=None):
+    """(minimum total error, widths) of min sum_g err[g][j_g] subject to
+    sum_g ALLOC_WIDTHS[j_g] * size[g] <= budget and ALLOC_WIDTHS[j_g] >= min_width[g],
+    by dynamic programming over the exact cost spent; None if infeasible."""
+    err = np.asarray(err, dtype=np.float64)
+    G = err.shape[0]
+    size = np.broadcast_to(np.asarray(size, dtype=np.int64), (G,))
+    dp = np.full(budget + 1, np.inf)
+    dp[0] = 0.0
+    choice = np.full((G, budget + 1), -1, dtype=np.int8)
+    for g in range(G):
+        new = np.full(budget + 1, np.inf)
+        for j, b in enumerate(ALLOC_WIDTHS):
+            if min_width is not None and b < min_width[g]:
+                continue
+            c = int(b * size[g])
+            if c > budget:
+                continue
+            cand = np.full(budget + 1, np.inf)
+            cand[c:] = dp[: budget + 1 - c] + err[g, j]
+            better = cand < new
+            new[better] = cand[better]
+            choice[g, better] = j
+        dp = new
+    c = int(np.argmin(dp))
+    if not np.isfinite(dp[c]):
+        return None
+    total = float(dp[c])
+    widths = [0] * G
+    for g in range(G - 1, -1, -1):
+        j = int(choice[g, c])
+        widths[g] = ALLOC_WIDTHS[j]
+        c -= ALLOC_WIDTHS[j] * int(size[g])
+    return total, widths
+
+
 def reference_layer(W: np.ndarray, widths):
     """Oracle's own quantize + pack of a layer: (codes, scales, qweight)."""
     codes, scales = quantize(W, widths)

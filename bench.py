@@ -197,6 +197,31 @@ def allocator_leg(exq, kept, nblk):
                         "the seeded schedule's budget (2.55 bpw per linear), its >= 6-bit groups kept" % nblk}
 
 
+def autotune_leg(exq, torch, layers, stream, Ms=(1, 4, 16, 32)):
+    """exq_autotune on block 0's seven linears at several row counts (20 warmup
+    and 200 timed runs per candidate, trimmed mean of the 5/16-11/16
+    quantiles); the choices are reset afterwards."""
+    from synth import BLOCK_SHAPES
+    names = ["decode16", "decode64", "prefill"]
+    out = {}
+    for M in Ms:
+        rows = []
+        for (name, K, N), lay in zip(BLOCK_SHAPES, layers):
+            x = torch.randn((M, K), device="cuda").half()
+            y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            choice, times = exq.exq_autotune(x.data_ptr(), M, lay.handle, y.data_ptr(), stream, 20, 200)
+            m = min(M, 16)   # exq_gemm's default: decode slices of 16 rows, this tile rule
+            default = 2 if (N // 64 >= 256 or (m >= 4 and N // 64 >= 128)) else 1
+            rows.append({"linear": name, "choice": names[choice - 1], "us": round(times[choice - 1], 2),
+                         "default_us": round(times[default - 1], 2),
+                         "candidates_us": [round(t, 2) for t in times]})
+            exq.exq_set_variant(lay.handle, M, 0)
+        out["M=%d" % M] = rows
+        log("autotune M=%d: %s" % (M, ", ".join("%s %s %.1f/%.1f us" % (r["linear"], r["choice"], r["us"], r["default_us"])
+                                                for r in rows)))
+    return out
+
+
 def gated_leg(exq, torch, layers, xs, M, nblk, steps, stream):
     """The 80 gate/up pairs of the stack: h = SiLU(x Wg^T) * (x Wu^T) per block
     as one exq_gemm_gated launch, against a two-linear plan plus torch's SiLU
@@ -337,6 +362,7 @@ def main():
     ap.add_argument("--no-stream-read", action="store_true", help="skip the plain streaming-read ceiling")
     ap.add_argument("--no-gated", action="store_true", help="skip the fused gate/up (SiLU) leg")
     ap.add_argument("--no-allocator", action="store_true", help="skip the host bit-allocation leg")
+    ap.add_argument("--no-autotune", action="store_true", help="skip the per-shape kernel-choice leg")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="run a plain device copy of this size (for counter calibration) and exit")
     args = ap.parse_args()
@@ -535,6 +561,10 @@ def main():
                           cbytes / 1e9, worst),
         }
 
+    tune = None
+    if not args.no_autotune:
+        tune = autotune_leg(exq, torch, layers[: len(BLOCK_SHAPES)], stream)
+
     alloc = None
     if not args.no_allocator and args.config == 5:
         alloc = allocator_leg(exq, kept if len(kept) == len(BLOCK_SHAPES) else None, nblk)
@@ -587,6 +617,7 @@ def main():
         "stream_read": read,
         "gated_gate_up": gated,
         "allocator": alloc,
+        "autotune": tune,
         "cpu_baseline": cpu,
         "prefill": prefill,
     }

@@ -154,10 +154,11 @@ void exq_layer_destroy(exq_layer_t layer);
 /* y = x * W_hat^T on `stream`.
  *   x  device, fp16 [M][K] row-major, 16-byte aligned
  *   y  device, fp16 [M][N] row-major, 16-byte aligned, must not overlap x
- *   M >= 1.  M <= 16 uses the decode kernel (scale factored per group, MFMA
- *   accumulation); larger M uses the prefill kernel (W_hat decoded exactly
- *   into fp16 MFMA operands, activation tiles in LDS).  Accumulation is fp32
- *   in both; output is fp16 RNE.
+ *   M >= 1.  By default M <= 64 uses the decode kernel (scale factored per
+ *   group, MFMA accumulation; one launch per 16 rows) and larger M the
+ *   prefill kernel (W_hat decoded exactly into fp16 MFMA operands,
+ *   activation tiles in LDS); exq_autotune / exq_set_variant can change the
+ *   choice for M <= 64.  Accumulation is fp32 in both; output is fp16 RNE.
  * Accuracy: |y - y_ref| <= 2e-3 * sum_k |x_k * w_hat_k| + 1e-5 per output,
  * y_ref the exact (fp64) product of the fp16 inputs. */
 exq_status exq_gemm(const void* x, int M, exq_layer_t layer, void* y, void* stream);
@@ -171,10 +172,10 @@ exq_status exq_gemm(const void* x, int M, exq_layer_t layer, void* y, void* stre
  *   x         device, fp16 [M][K] row-major, 16-byte aligned
  *   gate, up  handles of equal K and N
  *   h         device, fp16 [M][N] row-major, 16-byte aligned, must not overlap x
- *   M >= 1.  M <= 16: one launch; a workgroup streams the same 64 (or 16)
- *   columns of both linears and combines the two fp32 sums.  M > 16: the gate
- *   product is written to h by the prefill kernel, and the up product's
- *   epilogue reads it back (fp16) and writes SiLU(g) * u over it.
+ *   M >= 1.  M <= 64: one launch per 16 rows; a workgroup streams the same 64
+ *   (or 16) columns of both linears and combines the two fp32 sums.  M > 64:
+ *   the gate product is written to h by the prefill kernel, and the up
+ *   product's epilogue reads it back (fp16) and writes SiLU(g) * u over it.
  * Accuracy, with E_g, E_u the exq_gemm bounds of the two products and
  * g_ref, u_ref their exact values:
  *   |h - h_ref| <= 1.1 E_g (|u_ref| + E_u) + |SiLU(g_ref)| E_u
@@ -183,6 +184,46 @@ exq_status exq_gemm(const void* x, int M, exq_layer_t layer, void* y, void* stre
  * rounding).  Deterministic.  Errors: INVALID_ARG (NULL, misaligned,
  * overlapping, gate and up of different shapes), UNSUPPORTED, HIP. */
 exq_status exq_gemm_gated(const void* x, int M, exq_layer_t gate, exq_layer_t up, void* h, void* stream);
+
+/* ------------------------------------------------------ per-shape tuning */
+
+/* Kernel choices of exq_gemm for a layer at a row count M (1..64).  The
+ * exllamav2 report (可复用的模式与技巧 and 关键设计决策) times its kernel
+ * variants the first time a shape is seen -- 20 warmup and 200 timed runs
+ * each -- keeps the one with the lowest interquartile-style mean (the mean of
+ * the samples between the 5/16 and 11/16 quantiles) and caches the choice.
+ *   EXQ_VARIANT_DEFAULT   decode in 16-row slices, 64-column tiles when
+ *                         N/64 >= 256, or N/64 >= 128 and a slice has >= 4
+ *                         rows, else 16 (M <= 64 always takes this rule)
+ *   EXQ_VARIANT_DECODE16  decode, 16-column tiles (16-row slices of x if M > 16)
+ *   EXQ_VARIANT_DECODE64  decode, 64-column tiles (16-row slices of x if M > 16)
+ *   EXQ_VARIANT_PREFILL   prefill kernel (M > 16 only)
+ * Every choice meets exq_gemm's accuracy bound and is deterministic; two
+ * choices may round differently. */
+enum { EXQ_VARIANT_DEFAULT = 0, EXQ_VARIANT_DECODE16 = 1, EXQ_VARIANT_DECODE64 = 2, EXQ_VARIANT_PREFILL = 3 };
+
+/* Mean of the samples between the 5/16 and 11/16 quantiles of n >= 1 values
+ * (sorted; indices [5n/16, max(ceil(11n/16), 5n/16 + 1))).  Host; -1 on bad
+ * arguments. */
+double exq_trimmed_mean(const float* samples, int n);
+
+/* Time every choice that applies at M (decode 16 and 64 columns; also prefill
+ * when M > 16) on `stream` with x and y as for exq_gemm: `warmup` untimed and
+ * `reps` timed runs each, one HIP event pair per run; keep the choice with the
+ * lowest trimmed mean for (layer, M).  Later exq_gemm calls at this M use it.
+ * y ends up holding that choice's result.  Synchronizes with `stream`.
+ *   choice_out    host int or NULL: the chosen EXQ_VARIANT_*
+ *   times_us_out  host float [2] (M <= 16) or [3] (M > 16) or NULL: the trimmed
+ *                 means in microseconds, in variant order from DECODE16
+ * Not to be run while other work uses the layer at the same M.  Errors:
+ * INVALID_ARG (NULL, M outside 1..64, warmup < 0, reps outside 1..100000,
+ * misaligned or overlapping x/y), HIP, or a launch's own error. */
+exq_status exq_autotune(const void* x, int M, exq_layer_t layer, void* y, void* stream, int warmup, int reps,
+                        int* choice_out, float* times_us_out);
+
+/* Set the choice for (layer, M) directly (EXQ_VARIANT_DEFAULT restores the rule).
+ * Errors: INVALID_ARG (NULL, M outside 1..64, unknown variant, PREFILL at M <= 16). */
+exq_status exq_set_variant(exq_layer_t layer, int M, int variant);
 
 /* Materialize W_hat^T: w_out device, fp16 [K][N] row-major (w_out[k*N + n]),
  * bit-exact fp16_RNE((c - 2^(b-1)) * s).  Meant for testing and inspection. */

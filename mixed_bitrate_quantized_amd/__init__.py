@@ -64,10 +64,14 @@ def _load():
     lib.exq_stream_read.argtypes = [vp, u64, vp, i32, vp]
     lib.exq_gemm_gated.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.exq_group_errors.argtypes = [vp, i32, i32, i32, vp]
+    lib.exq_trimmed_mean.argtypes = [vp, i32]
+    lib.exq_trimmed_mean.restype = ctypes.c_double
+    lib.exq_autotune.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp]
+    lib.exq_set_variant.argtypes = [vp, i32, i32]
     lib.exq_allocate_widths.argtypes = [vp, vp, i32, ctypes.c_int64, vp, ctypes.c_uint64, ctypes.c_int64, vp, vp]
     for f in (lib.exq_pack, lib.exq_layer_create, lib.exq_gemm, lib.exq_dequant, lib.exq_plan_create,
               lib.exq_plan_run, lib.exq_stream_read, lib.exq_gemm_gated, lib.exq_group_errors,
-              lib.exq_allocate_widths):
+              lib.exq_allocate_widths, lib.exq_autotune, lib.exq_set_variant):
         f.restype = i32
     return lib
 
@@ -78,8 +82,11 @@ lib = _load()
 EXPORTED = (
     "exq_status_string", "exq_last_error", "exq_packed_bytes", "exq_pack", "exq_layer_create",
     "exq_layer_destroy", "exq_gemm", "exq_dequant", "exq_plan_create", "exq_plan_run", "exq_plan_destroy",
-    "exq_stream_read", "exq_gemm_gated", "exq_group_errors", "exq_allocate_widths",
+    "exq_stream_read", "exq_gemm_gated", "exq_group_errors", "exq_allocate_widths", "exq_trimmed_mean",
+    "exq_autotune", "exq_set_variant",
 )
+
+VARIANT_DEFAULT, VARIANT_DECODE16, VARIANT_DECODE64, VARIANT_PREFILL = 0, 1, 2, 3
 
 
 def _status_name(s: int) -> str:
@@ -171,6 +178,24 @@ def exq_allocate_widths(err: np.ndarray, size, budget: int, min_width=None, seed
                                    int(seed) & ((1 << 64) - 1), int(iterations), _np_ptr(out), ctypes.byref(total)),
            "exq_allocate_widths")
     return out, total.value
+
+
+def exq_trimmed_mean(samples) -> float:
+    s = np.ascontiguousarray(samples, dtype=np.float32)
+    return lib.exq_trimmed_mean(_np_ptr(s), s.size)
+
+
+def exq_autotune(x_ptr: int, M: int, handle: int, y_ptr: int, stream=None, warmup: int = 20, reps: int = 200):
+    """(chosen variant, trimmed-mean microseconds per candidate from DECODE16 on)."""
+    choice = ctypes.c_int()
+    times = np.zeros(3, dtype=np.float32)
+    _check(lib.exq_autotune(x_ptr, M, handle, y_ptr, _stream_ptr(stream), warmup, reps, ctypes.byref(choice),
+                            _np_ptr(times)), "exq_autotune")
+    return choice.value, times[: 3 if M > 16 else 2].tolist()
+
+
+def exq_set_variant(handle: int, M: int, variant: int) -> None:
+    _check(lib.exq_set_variant(handle, M, variant), "exq_set_variant")
 
 
 def exq_dequant(handle: int, w_ptr: int, stream=None) -> None:

@@ -456,9 +456,11 @@ LinearDev exq::linear_dev(const exq_layer* L, const void* x, void* y) {
 
 namespace {
 
-// Tile width for a single-linear launch: 64 columns when that still gives a
-// workgroup per CU, else 16.
-int tile_cols_for(int N) { return N / 64 >= 256 ? 64 : 16; }
+// Tile width for a single-linear launch of m <= 16 rows: 64 columns when
+// that still gives a workgroup per CU, or half that from 4 rows on (where the
+// wider tile's shared activation loads pay for the emptier machine: measured
+// 1.2x at 4 rows and 1.6x at 16 on 8192 columns); else 16.
+int tile_cols_for(int N, int m) { return (N / 64 >= 256 || (m >= 4 && N / 64 >= 128)) ? 64 : 16; }
 
 template <int MB, int TC, bool M1>
 void launch_decode_t(LinearDev d, int M, hipStream_t stream) {
@@ -498,7 +500,7 @@ void launch_gated_mb(const LinearDev& g, const LinearDev& u, int M, hipStream_t 
 }
 
 exq_status launch_decode(const LinearDev& d, int M, hipStream_t stream) {
-    if (tile_cols_for(d.N) == 64) launch_decode_mb<64>(d, M, stream);
+    if (tile_cols_for(d.N, M) == 64) launch_decode_mb<64>(d, M, stream);
     else launch_decode_mb<16>(d, M, stream);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? EXQ_OK : hip_fail(e, "decode launch");
@@ -530,17 +532,43 @@ extern int exq_prefill_tiles(const exq_layer* L, int M);
 extern exq_status exq_prefill_plan_launch(const LinearDev* d_list, const uint32_t* d_wg_map, int total_wgs, int M,
                                           hipStream_t stream);
 
-// Decode kernel over consecutive slices of at most 16 rows of x (any M).
-exq_status exq_decode_rows(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream) {
+// Decode kernel over consecutive slices of at most 16 rows of x (any M);
+// tc = 0: the tile width of tile_cols_for, else 16 or 64.
+exq_status exq_decode_rows(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream, int tc = 0) {
     for (int r0 = 0; r0 < M; r0 += kMaxDecodeM) {
         const int m = std::min(kMaxDecodeM, M - r0);
         const void* xs = static_cast<const uint16_t*>(x) + (size_t)r0 * L->K;
         void* ys = static_cast<uint16_t*>(y) + (size_t)r0 * L->N;
-        exq_status st = launch_decode(linear_dev(L, xs, ys), m, stream);
-        if (st != EXQ_OK) return st;
+        const LinearDev d = linear_dev(L, xs, ys);
+        if (tc == 0) {
+            exq_status st = launch_decode(d, m, stream);
+            if (st != EXQ_OK) return st;
+        } else {
+            if (tc == 64) launch_decode_mb<64>(d, m, stream);
+            else launch_decode_mb<16>(d, m, stream);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail(e, "decode launch");
+        }
     }
     return EXQ_OK;
 }
+
+namespace {
+
+// exq_gemm with a given kernel choice (kVarDefault: M <= kTuneMaxM decode in
+// 16-row slices with the tile_cols_for width, else prefill: a 256-row prefill
+// tile mostly empty is slower than a few decode slices, measured 3x at 32
+// rows on every 70B shape).
+exq_status run_variant(const exq_layer* L, const void* x, int M, void* y, hipStream_t s, int v) {
+    switch (v) {
+        case kVarDecode16: return exq_decode_rows(L, x, M, y, s, 16);
+        case kVarDecode64: return exq_decode_rows(L, x, M, y, s, 64);
+        case kVarPrefill: return exq_prefill_launch(L, x, M, y, s);
+        default: return M > kTuneMaxM ? exq_prefill_launch(L, x, M, y, s) : exq_decode_rows(L, x, M, y, s);
+    }
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -607,9 +635,79 @@ exq_status exq_gemm(const void* x, int M, exq_layer_t L, void* y, void* stream) 
     if (M < 1) return fail(EXQ_ERR_INVALID_ARG, "M=%d must be >= 1", M);
     if (!aligned16(x) || !aligned16(y)) return fail(EXQ_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
     if (overlap(x, 2 * (size_t)M * L->K, y, 2 * (size_t)M * L->N)) return fail(EXQ_ERR_INVALID_ARG, "y overlaps x");
+    const int v = M <= kTuneMaxM ? L->tuned[M].load(std::memory_order_relaxed) : kVarDefault;
+    return run_variant(L, x, M, y, static_cast<hipStream_t>(stream), v);
+}
+
+exq_status exq_set_variant(exq_layer_t L, int M, int variant) {
+    if (!L) return fail(EXQ_ERR_INVALID_ARG, "layer is NULL");
+    if (M < 1 || M > kTuneMaxM) return fail(EXQ_ERR_INVALID_ARG, "M=%d outside 1..%d", M, kTuneMaxM);
+    if (variant < 0 || variant >= kNumVariants) return fail(EXQ_ERR_INVALID_ARG, "variant %d", variant);
+    if (variant == kVarPrefill && M <= kMaxDecodeM)
+        return fail(EXQ_ERR_INVALID_ARG, "the prefill kernel serves M > %d", kMaxDecodeM);
+    L->tuned[M].store((uint8_t)variant, std::memory_order_relaxed);
+    return EXQ_OK;
+}
+
+exq_status exq_autotune(const void* x, int M, exq_layer_t L, void* y, void* stream, int warmup, int reps,
+                        int* choice_out, float* times_us_out) {
+    if (!L) return fail(EXQ_ERR_INVALID_ARG, "layer is NULL");
+    if (!x || !y) return fail(EXQ_ERR_INVALID_ARG, "NULL x or y");
+    if (M < 1 || M > kTuneMaxM) return fail(EXQ_ERR_INVALID_ARG, "M=%d outside 1..%d", M, kTuneMaxM);
+    if (warmup < 0 || reps < 1 || reps > 100000) return fail(EXQ_ERR_INVALID_ARG, "warmup=%d reps=%d", warmup, reps);
+    if (!aligned16(x) || !aligned16(y)) return fail(EXQ_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    if (overlap(x, 2 * (size_t)M * L->K, y, 2 * (size_t)M * L->N)) return fail(EXQ_ERR_INVALID_ARG, "y overlaps x");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (M > kMaxDecodeM) return exq_prefill_launch(L, x, M, y, s);
-    return exq_decode_rows(L, x, M, y, s);
+    std::vector<hipEvent_t> ev(2 * (size_t)reps, nullptr);
+    hipError_t e = hipSuccess;
+    for (auto& v : ev)
+        if ((e = hipEventCreate(&v)) != hipSuccess) break;
+    auto release = [&]() {
+        for (auto& v : ev)
+            if (v) (void)hipEventDestroy(v);
+    };
+    if (e != hipSuccess) {
+        release();
+        return hip_fail(e, "hipEventCreate");
+    }
+    const int first = kVarDecode16, last = M > kMaxDecodeM ? kVarPrefill : kVarDecode64;
+    std::vector<float> samples(reps);
+    int best = kVarDefault;
+    double best_t = 0.0;
+    for (int v = first; v <= last; ++v) {
+        exq_status st = EXQ_OK;
+        for (int i = 0; i < warmup && st == EXQ_OK; ++i) st = run_variant(L, x, M, y, s, v);
+        for (int i = 0; i < reps && st == EXQ_OK; ++i) {
+            (void)hipEventRecord(ev[2 * i], s);
+            st = run_variant(L, x, M, y, s, v);
+            (void)hipEventRecord(ev[2 * i + 1], s);
+        }
+        if (st != EXQ_OK) {
+            (void)hipStreamSynchronize(s);
+            release();
+            return st;
+        }
+        if ((e = hipEventSynchronize(ev[2 * reps - 1])) != hipSuccess) {
+            release();
+            return hip_fail(e, "hipEventSynchronize");
+        }
+        for (int i = 0; i < reps; ++i)
+            if ((e = hipEventElapsedTime(&samples[i], ev[2 * i], ev[2 * i + 1])) != hipSuccess) {
+                release();
+                return hip_fail(e, "hipEventElapsedTime");
+            }
+        const double t = exq_trimmed_mean(samples.data(), reps) * 1e3;   // microseconds
+        if (times_us_out) times_us_out[v - first] = (float)t;
+        if (best == kVarDefault || t < best_t) {
+            best = v;
+            best_t = t;
+        }
+    }
+    release();
+    L->tuned[M].store((uint8_t)best, std::memory_order_relaxed);
+    if (choice_out) *choice_out = best;
+    // Leave y holding the chosen kernel's result.
+    return run_variant(L, x, M, y, s, best);
 }
 
 exq_status exq_gemm_gated(const void* x, int M, exq_layer_t gate, exq_layer_t up, void* h, void* stream) {
@@ -623,19 +721,25 @@ exq_status exq_gemm_gated(const void* x, int M, exq_layer_t gate, exq_layer_t up
     if (overlap(x, 2 * (size_t)M * gate->K, h, 2 * (size_t)M * gate->N))
         return fail(EXQ_ERR_INVALID_ARG, "h overlaps x");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (M > kMaxDecodeM) {
+    if (M > kTuneMaxM) {
         // Gate product into h, then the up product's epilogue combines in place.
         exq_status st = exq_prefill_launch(gate, x, M, h, s);
         return st != EXQ_OK ? st : exq_prefill_launch_gated(up, x, M, h, s);
     }
-    // The tile width follows exq_gemm's rule.  (16-column tiles for the
-    // 28672-column feed-forward pair, which fills only 448 of the 512 slots
-    // with 64-column tiles, measured twice as slow.)
-    const LinearDev g = linear_dev(gate, x, h), u = linear_dev(up, x, nullptr);
-    if (tile_cols_for(gate->N) == 64) launch_gated_mb<64>(g, u, M, s);
-    else launch_gated_mb<16>(g, u, M, s);
-    hipError_t e = hipGetLastError();
-    return e == hipSuccess ? EXQ_OK : hip_fail(e, "gated decode launch");
+    // Decode in 16-row slices; the tile width follows exq_gemm's rule.  (16-
+    // column tiles for the 28672-column feed-forward pair, which fills only 448
+    // of the 512 slots with 64-column tiles, measured twice as slow.)
+    for (int r0 = 0; r0 < M; r0 += kMaxDecodeM) {
+        const int m = std::min(kMaxDecodeM, M - r0);
+        const void* xs = static_cast<const uint16_t*>(x) + (size_t)r0 * gate->K;
+        void* hs = static_cast<uint16_t*>(h) + (size_t)r0 * gate->N;
+        const LinearDev g = linear_dev(gate, xs, hs), u = linear_dev(up, xs, nullptr);
+        if (tile_cols_for(gate->N, m) == 64) launch_gated_mb<64>(g, u, m, s);
+        else launch_gated_mb<16>(g, u, m, s);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "gated decode launch");
+    }
+    return EXQ_OK;
 }
 
 exq_status exq_dequant(exq_layer_t L, void* w_out, void* stream) {

@@ -253,6 +253,16 @@ exq_status exq_pack(const float* W, int K, int N, int group_size, const uint8_t*
     return EXQ_OK;
 }
 
+double exq_trimmed_mean(const float* samples, int n) {
+    if (!samples || n < 1) return -1.0;
+    std::vector<float> s(samples, samples + n);
+    std::sort(s.begin(), s.end());
+    const int lo = (5 * n) / 16, hi = std::max((11 * n + 15) / 16, lo + 1);
+    double sum = 0.0;
+    for (int i = lo; i < hi; ++i) sum += s[i];
+    return sum / (hi - lo);
+}
+
 exq_status exq_group_errors(const float* W, int K, int N, int group_size, double* err_out) {
     if (!W || !err_out) return fail(EXQ_ERR_INVALID_ARG, "NULL buffer");
     if (K <= 0 || N <= 0 || K % kGroup) return fail(EXQ_ERR_INVALID_ARG, "bad shape K=%d N=%d", K, N);

@@ -1,6 +1,7 @@
 // Internal declarations shared by the host (HIP-free) and device halves of libexq.
 #pragma once
 
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
 #include <vector>
@@ -13,6 +14,10 @@ constexpr int kGroup = 128;     // input channels per group
 constexpr int kTileCols = 16;   // output columns per decode workgroup (lane % 16)
 constexpr int kWaves = 8;       // waves per decode workgroup, each takes a share of the groups
 constexpr int kMaxDecodeM = 16; // largest M served by the decode kernel
+constexpr int kTuneMaxM = 64;   // row counts a layer keeps a tuned kernel choice for
+
+// Kernel choices of exq_gemm (a layer's tuned entry for M, 0 = the default rule).
+enum Variant : uint8_t { kVarDefault = 0, kVarDecode16 = 1, kVarDecode64 = 2, kVarPrefill = 3, kNumVariants = 4 };
 
 // Records a message for exq_last_error() and returns `s`.
 exq_status fail(exq_status s, const char* fmt, ...);
@@ -56,4 +61,7 @@ struct exq_layer {
     uint32_t* d_order = nullptr;
     uint16_t* d_bounds = nullptr;
     uint16_t* d_runs = nullptr;
+    // Kernel choice per row count M (0 = default rule), set by exq_autotune or
+    // exq_set_variant; read without locking by exq_gemm.
+    std::atomic<uint8_t> tuned[exq::kTuneMaxM + 1] = {};
 };

@@ -116,3 +116,25 @@ def test_split_planner_balances_bytes():
     W = workloads.make_weight(spec)
     widths = workloads.make_widths(spec, W)
     assert int(widths.astype(int).sum()) == round(2.55 * spec.G)
+
+
+def test_trimmed_mean_definition():
+    """The autotune statistic: mean of the sorted samples between the 5/16 and
+    11/16 quantiles (for 16k samples exactly sorted[5k:11k])."""
+    import numpy as np
+    import mixed_bitrate_quantized_amd as exq
+    rng = np.random.default_rng(2)
+    for k in (1, 3, 12):
+        s = rng.normal(size=16 * k).astype(np.float32)
+        expect = np.sort(s)[5 * k:11 * k].astype(np.float64).mean()
+        assert abs(exq.exq_trimmed_mean(s) - expect) < 1e-6
+        assert abs(exq.exq_trimmed_mean(rng.permutation(s)) - expect) < 1e-6
+        # outliers in the top and bottom 5/16 do not move it
+        t = s.copy()
+        o = np.argsort(t)
+        t[o[-1]] = 1e9
+        t[o[0]] = -1e9
+        assert abs(exq.exq_trimmed_mean(t) - expect) < 1e-6
+    assert exq.exq_trimmed_mean([4.0]) == 4.0
+    assert exq.exq_trimmed_mean([2.0, 6.0]) == 4.0
+    assert exq.exq_trimmed_mean([]) == -1.0

@@ -32,7 +32,12 @@ def make_layer(exq, W, widths):
     np.testing.assert_array_equal(q, q_ref)
     np.testing.assert_array_equal(s, s_ref)
     N, K = W.shape
-    return exq.Layer(K, N, widths, q, s), oracle.dequant(codes, s_ref, widths)
+    layer = exq.Layer(K, N, widths, q, s)
+    # exq_gemm serves M <= 64 with the decode kernel by default; these tests
+    # are about the prefill kernel, so it is chosen for every M from 17 on.
+    for M in range(17, 65):
+        exq.exq_set_variant(layer.handle, M, exq.VARIANT_PREFILL)
+    return layer, oracle.dequant(codes, s_ref, widths)
 
 
 @pytest.mark.parametrize("N", [64, 320, 512])

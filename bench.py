@@ -197,6 +197,51 @@ def allocator_leg(exq, kept, nblk):
                         "the seeded schedule's budget (2.55 bpw per linear), its >= 6-bit groups kept" % nblk}
 
 
+def qs_leg(exq, torch, M, steps, stream, nblk=8):
+    """Decode with quantized group scales (4-bit codes + a column reference):
+    `nblk` 70B-shaped blocks (2.2 GB, well above the Infinity Cache) packed with
+    exq_pack_qs, one plan launch per block, rotating over the blocks."""
+    from synth import BLOCK_SHAPES, workloads
+    specs = workloads.linears(5)[: nblk * len(BLOCK_SHAPES)]
+    layers, xs, ys, nbytes = [], [], [], 0
+    for spec in specs:
+        W = workloads.make_weight(spec)
+        widths = workloads.make_widths(spec, W)
+        q, qsc, ref = exq.exq_pack_qs(W, widths)
+        layers.append(exq.Layer(spec.K, spec.N, widths, q, qsc, ref=ref))
+        xs.append(torch.from_numpy(workloads.make_x(spec, M)).cuda())
+        ys.append(torch.empty((M, spec.N), dtype=torch.float16, device="cuda"))
+        G = spec.K // 128
+        nbytes += q.size + qsc.size + 2 * spec.N + 5 * G + 2 * M * spec.K + 2 * M * spec.N
+    plans = [exq.Plan(layers[b * 7:(b + 1) * 7], xs[b * 7:(b + 1) * 7], ys[b * 7:(b + 1) * 7], M) for b in range(nblk)]
+
+    def step():
+        for p in plans:
+            p.run(stream)
+
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(steps, 40)
+    e0.record(stream)
+    for _ in range(reps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_block = e0.elapsed_time(e1) * 1e3 / (reps * nblk)
+    for p in plans:
+        p.close()
+    for l in layers:
+        l.close()
+    per_block = nbytes / nblk
+    log("quantized scales: %.1f us per block, %.0f B per block" % (us_block, per_block))
+    return {"workload": "%d llama3-70b-shaped blocks, 2.55 bpw, 4-bit group scale codes, M=%d, one plan per block" % (nblk, M),
+            "us_per_block": round(us_block, 2), "bytes_per_block": int(per_block),
+            "GB/s": round(per_block / (us_block * 1e-6) / 1e9, 1),
+            "ms_per_step_80_blocks_equivalent": round(us_block * 80 / 1e3, 4)}
+
+
 def autotune_leg(exq, torch, layers, stream, Ms=(1, 4, 16, 32)):
     """exq_autotune on block 0's seven linears at several row counts (20 warmup
     and 200 timed runs per candidate, trimmed mean of the 5/16-11/16
@@ -363,6 +408,7 @@ def main():
     ap.add_argument("--no-gated", action="store_true", help="skip the fused gate/up (SiLU) leg")
     ap.add_argument("--no-allocator", action="store_true", help="skip the host bit-allocation leg")
     ap.add_argument("--no-autotune", action="store_true", help="skip the per-shape kernel-choice leg")
+    ap.add_argument("--no-qs", action="store_true", help="skip the quantized-scale decode leg")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="run a plain device copy of this size (for counter calibration) and exit")
     args = ap.parse_args()
@@ -561,6 +607,11 @@ def main():
                           cbytes / 1e9, worst),
         }
 
+    qsres = None
+    if not args.no_qs and args.config == 5:
+        qsres = qs_leg(exq, torch, M, args.steps, stream)
+        qsres["fp16_scales_us_per_block"] = round(ms_step * 1e3 / nblk, 2)
+
     tune = None
     if not args.no_autotune:
         tune = autotune_leg(exq, torch, layers[: len(BLOCK_SHAPES)], stream)
@@ -618,6 +669,7 @@ def main():
         "gated_gate_up": gated,
         "allocator": alloc,
         "autotune": tune,
+        "quantized_scales": qsres,
         "cpu_baseline": cpu,
         "prefill": prefill,
     }

@@ -92,6 +92,26 @@ size_t exq_packed_bytes(int K, int N, int group_size, const uint8_t* widths);
 exq_status exq_pack(const float* W, int K, int N, int group_size, const uint8_t* widths,
                     void* qweight_out, uint16_t* scales_out);
 
+/* Quantize and pack a layer with quantized group scales (the exllamav2
+ * report's 4-bit second-level scale code, section 创新之处, with a scan of
+ * candidate scales by their error; the formula printed there is garbled, so
+ * this is our specification).  Per column n, R[n] = fp16_RNE(max over the
+ * column of |w|).  Per (group g, column n), with amax the group's max|w| and
+ * qmax = 2^(b-1)-1:
+ *   scale(q) = fp16_RNE(fp32(t * fp32(1/qmax))),  t = R (q+1)^2 / 256 (exact)
+ *   qc = clamp(ceil(16 * sqrtf(amax / R)), 1, 16) - 1   (fp32, IEEE; 0 if R = 0)
+ *   q  = qc, or qc - 1 if its codes give a strictly smaller squared error
+ *        sum_i (w_i - w_hat_i)^2 (double, i ascending)
+ * and the codes of exq_pack at scale(q).  Scale storage drops from 16 to 4
+ * bits per (group, column) plus 16 per column.
+ *   qweight_out host, exq_packed_bytes() bytes (EXQ1, as exq_pack)
+ *   qscale_out  host, uint8 [K/128][N/2]: byte g*(N/2) + n/2 holds q of column n
+ *               in its low nibble for even n, its high nibble for odd n
+ *   ref_out     host, fp16 [N]: R
+ * N must be even.  Errors as exq_pack. */
+exq_status exq_pack_qs(const float* W, int K, int N, int group_size, const uint8_t* widths, void* qweight_out,
+                       uint8_t* qscale_out, uint16_t* ref_out);
+
 /* ------------------------------------------------- bit-width allocation */
 
 /* The offline measurement and optimizer of the exllamav2 report (sections
@@ -146,6 +166,19 @@ exq_status exq_allocate_widths(const double* err, const int32_t* size, int G, in
  * not fit in LDS), OOM, HIP. */
 exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_host,
                             const void* d_qweight, const void* d_scales, exq_layer_t* out);
+
+/* A layer stored with quantized scales (exq_pack_qs): d_qscale (uint8
+ * [K/128][N/2]) and d_ref (fp16 [N]) replace d_scales, both borrowed and
+ * 16-byte aligned.  The decode kernels read the 4-bit codes (a quarter of the
+ * scale bytes).  The prefill and dequant kernels read fp16 scales: the first
+ * call that needs them (exq_gemm or exq_gemm_gated above 64 rows, or with the
+ * prefill choice; exq_dequant; a prefill plan's creation) allocates the
+ * expansion, 2*(K/128)*N bytes owned by the handle, fills it on that call's
+ * stream and waits for it once.  A layer only ever decoded never holds it.
+ * Every entry point accepts such a handle; a decode plan and a gated pair
+ * need one storage kind for all their linears.  Errors as exq_layer_create. */
+exq_status exq_layer_create_qs(int K, int N, int group_size, const uint8_t* widths_host, const void* d_qweight,
+                               const void* d_qscale, const void* d_ref, exq_layer_t* out);
 
 /* Release a handle and what it owns (not the borrowed buffers).  NULL is a no-op.
  * The caller must make sure no launched work still uses the handle. */

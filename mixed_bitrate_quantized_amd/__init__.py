@@ -64,6 +64,8 @@ def _load():
     lib.exq_stream_read.argtypes = [vp, u64, vp, i32, vp]
     lib.exq_gemm_gated.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.exq_group_errors.argtypes = [vp, i32, i32, i32, vp]
+    lib.exq_pack_qs.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.exq_layer_create_qs.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.POINTER(vp)]
     lib.exq_trimmed_mean.argtypes = [vp, i32]
     lib.exq_trimmed_mean.restype = ctypes.c_double
     lib.exq_autotune.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp]
@@ -71,7 +73,8 @@ def _load():
     lib.exq_allocate_widths.argtypes = [vp, vp, i32, ctypes.c_int64, vp, ctypes.c_uint64, ctypes.c_int64, vp, vp]
     for f in (lib.exq_pack, lib.exq_layer_create, lib.exq_gemm, lib.exq_dequant, lib.exq_plan_create,
               lib.exq_plan_run, lib.exq_stream_read, lib.exq_gemm_gated, lib.exq_group_errors,
-              lib.exq_allocate_widths, lib.exq_autotune, lib.exq_set_variant):
+              lib.exq_allocate_widths, lib.exq_autotune, lib.exq_set_variant, lib.exq_pack_qs,
+              lib.exq_layer_create_qs):
         f.restype = i32
     return lib
 
@@ -83,7 +86,7 @@ EXPORTED = (
     "exq_status_string", "exq_last_error", "exq_packed_bytes", "exq_pack", "exq_layer_create",
     "exq_layer_destroy", "exq_gemm", "exq_dequant", "exq_plan_create", "exq_plan_run", "exq_plan_destroy",
     "exq_stream_read", "exq_gemm_gated", "exq_group_errors", "exq_allocate_widths", "exq_trimmed_mean",
-    "exq_autotune", "exq_set_variant",
+    "exq_autotune", "exq_set_variant", "exq_pack_qs", "exq_layer_create_qs",
 )
 
 VARIANT_DEFAULT, VARIANT_DECODE16, VARIANT_DECODE64, VARIANT_PREFILL = 0, 1, 2, 3
@@ -135,6 +138,32 @@ def exq_pack(W: np.ndarray, widths, group_size: int = GROUP):
     s = np.empty((K // group_size, N), dtype=np.uint16)
     _check(lib.exq_pack(_np_ptr(W), K, N, group_size, _np_ptr(w), _np_ptr(q), _np_ptr(s)), "exq_pack")
     return q, s
+
+
+def exq_pack_qs(W: np.ndarray, widths, group_size: int = GROUP):
+    """Host quantize + pack with quantized group scales.  W fp32 [N][K] ->
+    (qweight uint8 bytes, 4-bit scale codes uint8 [G][N/2], column references fp16 bits uint16 [N])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    w = np.ascontiguousarray(widths, dtype=np.uint8)
+    nbytes = exq_packed_bytes(K, N, w, group_size)
+    if nbytes == 0:
+        _check(lib.exq_pack_qs(_np_ptr(W), K, N, group_size, _np_ptr(w), None, None, None), "exq_pack_qs")
+    q = np.empty(nbytes, dtype=np.uint8)
+    qs = np.empty((K // group_size, N // 2), dtype=np.uint8)
+    ref = np.empty(N, dtype=np.uint16)
+    _check(lib.exq_pack_qs(_np_ptr(W), K, N, group_size, _np_ptr(w), _np_ptr(q), _np_ptr(qs), _np_ptr(ref)),
+           "exq_pack_qs")
+    return q, qs, ref
+
+
+def exq_layer_create_qs(K: int, N: int, widths, d_qweight: int, d_qscale: int, d_ref: int,
+                        group_size: int = GROUP) -> int:
+    w = np.ascontiguousarray(widths, dtype=np.uint8)
+    h = ctypes.c_void_p()
+    _check(lib.exq_layer_create_qs(K, N, group_size, _np_ptr(w), d_qweight, d_qscale, d_ref, ctypes.byref(h)),
+           "exq_layer_create_qs")
+    return h.value
 
 
 def exq_layer_create(K: int, N: int, widths, d_qweight: int, d_scales: int, group_size: int = GROUP) -> int:
@@ -229,18 +258,29 @@ def exq_plan_destroy(plan: int) -> None:
 class Layer:
     """A packed layer resident on the GPU: owns its torch buffers and the handle."""
 
-    def __init__(self, K: int, N: int, widths, qweight: np.ndarray, scales: np.ndarray, device="cuda"):
+    def __init__(self, K: int, N: int, widths, qweight: np.ndarray, scales: np.ndarray, device="cuda", ref=None):
+        """fp16 scales [G][N]; or, with `ref` (fp16 bits [N]), 4-bit scale codes [G][N/2] in `scales`."""
         import torch
         self.K, self.N = K, N
         self.widths = np.ascontiguousarray(widths, dtype=np.uint8)
         self.qweight = torch.from_numpy(np.ascontiguousarray(qweight)).to(device)
-        self.scales = torch.from_numpy(np.ascontiguousarray(scales).view(np.int16)).to(device)
-        self.handle = exq_layer_create(K, N, self.widths, self.qweight.data_ptr(), self.scales.data_ptr())
+        if ref is None:
+            self.scales = torch.from_numpy(np.ascontiguousarray(scales).view(np.int16)).to(device)
+            self.ref = None
+            self.handle = exq_layer_create(K, N, self.widths, self.qweight.data_ptr(), self.scales.data_ptr())
+        else:
+            self.scales = torch.from_numpy(np.ascontiguousarray(scales, dtype=np.uint8)).to(device)
+            self.ref = torch.from_numpy(np.ascontiguousarray(ref).view(np.int16)).to(device)
+            self.handle = exq_layer_create_qs(K, N, self.widths, self.qweight.data_ptr(), self.scales.data_ptr(),
+                                              self.ref.data_ptr())
 
     @classmethod
-    def from_weight(cls, W: np.ndarray, widths, device="cuda"):
-        q, s = exq_pack(W, widths)
+    def from_weight(cls, W: np.ndarray, widths, device="cuda", quantized_scales: bool = False):
         N, K = W.shape
+        if quantized_scales:
+            q, qs, ref = exq_pack_qs(W, widths)
+            return cls(K, N, widths, q, qs, device, ref=ref)
+        q, s = exq_pack(W, widths)
         return cls(K, N, widths, q, s, device)
 
     @property

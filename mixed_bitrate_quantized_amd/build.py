@@ -37,22 +37,30 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source (always) and link libexq.so next to this file."""
+    """Compile every source (always, all at once) and link libexq.so next to this file."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
+    jobs = []
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        _run(["g++", "-O2", "-fPIC", "-fopenmp", "-std=c++17", "-ffp-contract=off", "-Wall",
-              "-c", os.path.join(CSRC, src), "-o", obj])
-        objs.append(obj)
+        jobs.append((obj, ["g++", "-O2", "-fPIC", "-fopenmp", "-std=c++17", "-ffp-contract=off", "-Wall",
+                           "-c", os.path.join(CSRC, src), "-o", obj]))
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        out = _run([hipcc()] + HIPCC_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
-        if verbose and out.strip():
+        jobs.append((obj, [hipcc()] + HIPCC_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]))
+    procs = [(cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+             for _, cmd in jobs]
+    failed = None
+    for cmd, p in procs:
+        out = "\n".join(l for l in p.communicate()[0].splitlines() if "not a recognized feature" not in l)
+        if p.returncode != 0:
+            sys.stderr.write(out + "\n")
+            failed = failed or cmd
+        elif verbose and out.strip():
             print(out)
-        objs.append(obj)
+    if failed:
+        raise RuntimeError("build step failed: " + " ".join(failed))
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + ["-lgomp"])
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in jobs] + ["-lgomp"])
     os.replace(tmp, LIB)
     return LIB
 

@@ -68,8 +68,31 @@ __device__ __forceinline__ void load_group_words(__amdgpu_buffer_rsrc_t rw, uint
 
 struct DecodeCtx {
     int M, lane, q, n;
-    __amdgpu_buffer_rsrc_t rw, rs;   // weight and scale buffers
+    float ref;                       // quantized scales: the column's range reference R
+    __amdgpu_buffer_rsrc_t rw, rs;   // weight and scale (or 4-bit scale code) buffers
 };
+
+// The group scale.  fp16 scales: the loaded value.  Quantized scales (QS):
+// the loaded byte holds the column's 4-bit code q in its low (even column)
+// or high (odd column) nibble, and s = fp16_RNE(fp32(t * fp32(1/(2^(b-1)-1))))
+// with t = R (q+1)^2 / 256, exact in fp32.
+template <int B, bool QS>
+__device__ __forceinline__ float group_scale(const DecodeCtx& c, uint16_t raw) {
+    if constexpr (!QS) {
+        return (float)__builtin_bit_cast(_Float16, raw);
+    } else {
+        // Two roundings, as specified: the fp32 product, then fp16.  The
+        // empty asm (no side effects) hands the product over in a register;
+        // without it the product and the conversion fuse into one
+        // mixed-precision multiply (v_fma_mixlo_f16) that rounds once, to fp16.
+        constexpr float inv = 1.0f / (float)((1 << (B - 1)) - 1);
+        const int q1 = (int)((raw >> (4 * (c.n & 1))) & 15u) + 1;
+        const float t = c.ref * (float)(q1 * q1) * 0.00390625f;
+        float u = t * inv;
+        asm("" : "+v"(u));
+        return (float)(_Float16)u;
+    }
+}
 
 template <int TC> struct Tile {
     static constexpr int NQ = TC == 64 ? 4 : 1;     // K-quarters of a group per lane
@@ -116,7 +139,7 @@ __device__ __forceinline__ float act_sum_row(float lane_sum, const DecodeCtx& c,
     else return __shfl(lane_sum, 16 * c.q + r);
 }
 
-template <int B, int MB, int TC, bool M1>
+template <int B, int MB, int TC, bool M1, bool QS>
 __device__ __forceinline__ void group_compute(const DecodeCtx& c, const uint32_t (&Q)[B * Tile<TC>::NQ],
                                               const u4v (&X)[MB], uint16_t s16, float (&yacc)[MB][4]) {
     using TT = Tile<TC>;
@@ -138,7 +161,7 @@ __device__ __forceinline__ void group_compute(const DecodeCtx& c, const uint32_t
             acc[t][rb] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, acc[t][rb], TT::CBSZ, U >> 1, 0);
         }
     });
-    const float s = (float)__builtin_bit_cast(_Float16, s16);
+    const float s = group_scale<B, QS>(c, s16);
     constexpr float z = (float)(1 << (B - 1));
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
@@ -167,7 +190,7 @@ template <int B, int TC> struct Depth {
 // operands, in that order -- so each wait is a compile-time count.  Steps
 // past the end of the run load from an out-of-range buffer offset: they
 // keep the count fixed, return zeros and cost no memory traffic.
-template <int B, int MB, int TC, bool M1>
+template <int B, int MB, int TC, bool M1, bool QS>
 __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c, const uint32_t* ord, int cnt,
                                           float (&yacc)[MB][4]) {
     constexpr int DEPTH = Depth<B, TC>::value;
@@ -184,8 +207,13 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
         const uint32_t col = valid ? 16u * ((uint32_t)L.N * P + (uint32_t)c.n) : kBufOOB;
         if constexpr (TC == 64) load_group_words<B>(c.rw, col, N16, Qd);
         else load_quarter<B>(c.rw, col, N16, c.q, Qd);
-        const uint32_t soff = valid ? 2u * (g * (uint32_t)L.N + (uint32_t)c.n) : kBufOOB;
-        Sd = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(c.rs, soff, 0, 0);
+        if constexpr (QS) {
+            const uint32_t soff = valid ? g * ((uint32_t)L.N >> 1) + ((uint32_t)c.n >> 1) : kBufOOB;
+            Sd = (uint16_t)__builtin_amdgcn_raw_buffer_load_b8(c.rs, soff, 0, 0);
+        } else {
+            const uint32_t soff = valid ? 2u * (g * (uint32_t)L.N + (uint32_t)c.n) : kBufOOB;
+            Sd = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(c.rs, soff, 0, 0);
+        }
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) Xd[rb] = load_act<TC>(L, c, (int)g, rb);
     };
@@ -203,7 +231,7 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
                 return;
             }
             issue(i + k + DEPTH - 1, Q[nk], S[nk], X[nk]);
-            group_compute<B, MB, TC, M1>(c, Q[k], X[k], S[k], yacc);
+            group_compute<B, MB, TC, M1, QS>(c, Q[k], X[k], S[k], yacc);
         });
     }
 }
@@ -212,7 +240,7 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
 // wave starts streaming at once and only the final reduction is shared.
 // decode_stream leaves each wave's partial sums in red (kWaves x M x TC
 // fp32); after a workgroup barrier the waves are added in order.
-template <int MB, int TC, bool M1>
+template <int MB, int TC, bool M1, bool QS>
 __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int M, float* red) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -222,7 +250,13 @@ __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int 
     c.q = TC == 64 ? 0 : lane >> 4;
     c.n = tile * TC + (TC == 64 ? lane : (lane & 15));
     c.rw = buffer_rsrc(L.qweight, L.qbytes);
-    c.rs = buffer_rsrc(L.scales, L.sbytes);
+    if constexpr (QS) {
+        c.rs = buffer_rsrc(L.qscale, L.qsbytes);
+        c.ref = (float)__builtin_bit_cast(_Float16, gptr<uint16_t>(L.ref)[c.n]);
+    } else {
+        c.rs = buffer_rsrc(L.scales, L.sbytes);
+        c.ref = 0.0f;
+    }
 
     float yacc[MB][4];
 #pragma unroll
@@ -233,12 +267,12 @@ __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int 
         const uint32_t* ord = L.order + gptr<uint16_t>(L.bounds)[wave];
         const EXQ_GLOBAL uint16_t* cnt = gptr<uint16_t>(L.runs) + wave * kNumWidths;
         int k;
-        if ((k = cnt[0]) > 0) { run_width<2, MB, TC, M1>(L, c, ord, k, yacc); ord += k; }
-        if ((k = cnt[1]) > 0) { run_width<3, MB, TC, M1>(L, c, ord, k, yacc); ord += k; }
-        if ((k = cnt[2]) > 0) { run_width<4, MB, TC, M1>(L, c, ord, k, yacc); ord += k; }
-        if ((k = cnt[3]) > 0) { run_width<5, MB, TC, M1>(L, c, ord, k, yacc); ord += k; }
-        if ((k = cnt[4]) > 0) { run_width<6, MB, TC, M1>(L, c, ord, k, yacc); ord += k; }
-        if ((k = cnt[5]) > 0) { run_width<8, MB, TC, M1>(L, c, ord, k, yacc); }
+        if ((k = cnt[0]) > 0) { run_width<2, MB, TC, M1, QS>(L, c, ord, k, yacc); ord += k; }
+        if ((k = cnt[1]) > 0) { run_width<3, MB, TC, M1, QS>(L, c, ord, k, yacc); ord += k; }
+        if ((k = cnt[2]) > 0) { run_width<4, MB, TC, M1, QS>(L, c, ord, k, yacc); ord += k; }
+        if ((k = cnt[3]) > 0) { run_width<5, MB, TC, M1, QS>(L, c, ord, k, yacc); ord += k; }
+        if ((k = cnt[4]) > 0) { run_width<6, MB, TC, M1, QS>(L, c, ord, k, yacc); ord += k; }
+        if ((k = cnt[5]) > 0) { run_width<8, MB, TC, M1, QS>(L, c, ord, k, yacc); }
     }
 
     // TC = 16: quarters ((q0 + q1) + (q2 + q3)) in every lane of a column.
@@ -265,9 +299,9 @@ __device__ __forceinline__ float tile_sum(const float* red, int M, int m, int co
     return v;
 }
 
-template <int MB, int TC, bool M1>
+template <int MB, int TC, bool M1, bool QS>
 __device__ __forceinline__ void decode_wg(const LinearDev& L, int tile, int M, float* red) {
-    decode_stream<MB, TC, M1>(L, tile, M, red);
+    decode_stream<MB, TC, M1, QS>(L, tile, M, red);
     __syncthreads();
     for (int t = threadIdx.x; t < M * TC; t += kWaves * 64) {
         const int m = t / TC, col = t % TC;
@@ -282,11 +316,11 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // A gate/up pair sharing x: every wave streams its share of the gate
 // linear's groups, then the same share of the up linear's, into two sets of
 // partials; the workgroup then writes h = SiLU(g) * u for its TC columns.
-template <int MB, int TC, bool M1>
+template <int MB, int TC, bool M1, bool QS>
 __global__ __launch_bounds__(kWaves * 64) void gated_decode_kernel(LinearDev G, LinearDev U, int M) {
     __shared__ float red[2][kWaves * 4 * MB * TC];
-    decode_stream<MB, TC, M1>(G, blockIdx.x, M, red[0]);
-    decode_stream<MB, TC, M1>(U, blockIdx.x, M, red[1]);
+    decode_stream<MB, TC, M1, QS>(G, blockIdx.x, M, red[0]);
+    decode_stream<MB, TC, M1, QS>(U, blockIdx.x, M, red[1]);
     __syncthreads();
     for (int t = threadIdx.x; t < M * TC; t += kWaves * 64) {
         const int m = t / TC, col = t % TC;
@@ -295,13 +329,13 @@ __global__ __launch_bounds__(kWaves * 64) void gated_decode_kernel(LinearDev G, 
     }
 }
 
-template <int MB, int TC, bool M1>
+template <int MB, int TC, bool M1, bool QS>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(LinearDev L, int M) {
     __shared__ float red[kWaves * 4 * MB * TC];
-    decode_wg<MB, TC, M1>(L, blockIdx.x, M, red);
+    decode_wg<MB, TC, M1, QS>(L, blockIdx.x, M, red);
 }
 
-template <int MB, bool M1>
+template <int MB, bool M1, bool QS>
 __global__ __launch_bounds__(kWaves * 64) void decode_plan_kernel(const LinearDev* __restrict__ list,
                                                                    const uint32_t* __restrict__ wg_map, int M) {
     __shared__ float red[kWaves * 4 * MB * 64];
@@ -315,7 +349,30 @@ __global__ __launch_bounds__(kWaves * 64) void decode_plan_kernel(const LinearDe
         for (int i = 0; i < (int)(sizeof(LinearDev) / 4); ++i)
             dst[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)src[i]);   // uniform: SGPRs
     }
-    decode_wg<MB, 64, M1>(L, (int)(e >> 16), M, red);
+    decode_wg<MB, 64, M1, QS>(L, (int)(e >> 16), M, red);
+}
+
+// ------------------------------------------------- quantized scale expansion
+
+// s[g][n] = fp16_RNE(fp32(t * fp32(1/(2^(b-1)-1)))), t = R[n] (q+1)^2 / 256 with
+// q the 4-bit code of (g, n): the fp16 scales the prefill and dequant kernels
+// read for a layer stored with quantized scales.  One thread per (g, n).
+__global__ __launch_bounds__(256) void expand_qs_kernel(const uint8_t* __restrict__ qscale,
+                                                        const uint16_t* __restrict__ ref,
+                                                        const uint32_t* __restrict__ meta, int G, int N,
+                                                        uint16_t* __restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)G * N) return;
+    const int g = (int)(i / N), n = (int)(i % N);
+    const int b = (int)(gptr<uint32_t>(meta)[g] & 15u);
+    const float inv = b == 2 ? 1.0f / 1.0f : b == 3 ? 1.0f / 3.0f : b == 4 ? 1.0f / 7.0f
+                    : b == 5 ? 1.0f / 15.0f : b == 6 ? 1.0f / 31.0f : 1.0f / 127.0f;
+    const int q1 = (int)((gptr<uint8_t>(qscale)[(size_t)g * (N / 2) + n / 2] >> (4 * (n & 1))) & 15u) + 1;
+    const float R = (float)__builtin_bit_cast(_Float16, gptr<uint16_t>(ref)[n]);
+    const float t = R * (float)(q1 * q1) * 0.00390625f;
+    float u = t * inv;
+    asm("" : "+v"(u));   // the fp32 product, then fp16 (see group_scale)
+    *gptr_w<uint16_t>(out + i) = __builtin_bit_cast(uint16_t, (_Float16)u);
 }
 
 // ---------------------------------------------------------------- dequant
@@ -414,6 +471,7 @@ constexpr uint32_t kPlanEmpty = 0xFFFFFFFFu;  // prefill plan entry of a workgro
 struct exq_plan {
     int count = 0, M = 1, total_wgs = 0;
     bool prefill = false;   // M > 16: prefill tiles, else decode column tiles
+    bool qs = false;        // decode plan of layers with quantized scales
     LinearDev* d_list = nullptr;
     uint32_t* d_wg_map = nullptr;
 };
@@ -436,7 +494,7 @@ exq_status hip_fail(hipError_t e, const char* what) {
 LinearDev exq::linear_dev(const exq_layer* L, const void* x, void* y) {
     LinearDev d;
     d.qweight = static_cast<const uint8_t*>(L->qweight);
-    d.scales = static_cast<const uint16_t*>(L->scales);
+    d.scales = L->qs ? L->d_scales_own.load(std::memory_order_acquire) : static_cast<const uint16_t*>(L->scales);
     d.meta = L->d_meta;
     d.order = L->d_order;
     d.bounds = L->d_bounds;
@@ -451,6 +509,10 @@ LinearDev exq::linear_dev(const exq_layer* L, const void* x, void* y) {
     for (int g = 0; g < L->G; ++g) words += L->widths[g];
     d.qbytes = (uint32_t)(16 * words * (size_t)L->N);
     d.sbytes = (uint32_t)(2 * (size_t)L->G * (size_t)L->N);
+    d.qscale = static_cast<const uint8_t*>(L->qscale);
+    d.ref = static_cast<const uint16_t*>(L->ref);
+    d.qsbytes = L->qs ? (uint32_t)((size_t)L->G * (size_t)(L->N / 2)) : 0u;
+    d.qs = L->qs ? 1 : 0;
     return d;
 }
 
@@ -465,7 +527,8 @@ int tile_cols_for(int N, int m) { return (N / 64 >= 256 || (m >= 4 && N / 64 >= 
 template <int MB, int TC, bool M1>
 void launch_decode_t(LinearDev d, int M, hipStream_t stream) {
     d.tiles = d.N / TC;
-    hipLaunchKernelGGL((decode_kernel<MB, TC, M1>), dim3(d.tiles), dim3(kWaves * 64), 0, stream, d, M);
+    if (d.qs) hipLaunchKernelGGL((decode_kernel<MB, TC, M1, true>), dim3(d.tiles), dim3(kWaves * 64), 0, stream, d, M);
+    else hipLaunchKernelGGL((decode_kernel<MB, TC, M1, false>), dim3(d.tiles), dim3(kWaves * 64), 0, stream, d, M);
 }
 
 template <int TC>
@@ -483,7 +546,11 @@ void launch_decode_mb(const LinearDev& d, int M, hipStream_t stream) {
 
 template <int MB, int TC, bool M1>
 void launch_gated_t(LinearDev g, LinearDev u, int M, hipStream_t stream) {
-    hipLaunchKernelGGL((gated_decode_kernel<MB, TC, M1>), dim3(g.N / TC), dim3(kWaves * 64), 0, stream, g, u, M);
+    if (g.qs)
+        hipLaunchKernelGGL((gated_decode_kernel<MB, TC, M1, true>), dim3(g.N / TC), dim3(kWaves * 64), 0, stream, g, u, M);
+    else
+        hipLaunchKernelGGL((gated_decode_kernel<MB, TC, M1, false>), dim3(g.N / TC), dim3(kWaves * 64), 0, stream, g, u,
+                           M);
 }
 
 template <int TC>
@@ -508,8 +575,12 @@ exq_status launch_decode(const LinearDev& d, int M, hipStream_t stream) {
 
 template <int MB, bool M1>
 void launch_plan_t(const exq_plan* P, hipStream_t s) {
-    hipLaunchKernelGGL((decode_plan_kernel<MB, M1>), dim3(P->total_wgs), dim3(kWaves * 64), 0, s, P->d_list,
-                       P->d_wg_map, P->M);
+    if (P->qs)
+        hipLaunchKernelGGL((decode_plan_kernel<MB, M1, true>), dim3(P->total_wgs), dim3(kWaves * 64), 0, s, P->d_list,
+                           P->d_wg_map, P->M);
+    else
+        hipLaunchKernelGGL((decode_plan_kernel<MB, M1, false>), dim3(P->total_wgs), dim3(kWaves * 64), 0, s, P->d_list,
+                           P->d_wg_map, P->M);
 }
 
 void launch_plan(const exq_plan* P, hipStream_t s) {
@@ -553,18 +624,46 @@ exq_status exq_decode_rows(const exq_layer* L, const void* x, int M, void* y, hi
     return EXQ_OK;
 }
 
+// The fp16 scales the prefill and dequant kernels read.  A layer with
+// quantized scales makes them on the first call that needs them: allocated,
+// filled on `stream` and waited for before the pointer is published, so
+// calls on other streams never see a partial table.
+exq_status ensure_scales(exq_layer* L, hipStream_t stream) {
+    if (!L->qs || L->d_scales_own.load(std::memory_order_acquire)) return EXQ_OK;
+    std::lock_guard<std::mutex> lock(L->expand_mu);
+    if (L->d_scales_own.load(std::memory_order_acquire)) return EXQ_OK;
+    const size_t n = (size_t)L->G * L->N;
+    uint16_t* d = nullptr;
+    hipError_t e;
+    if ((e = hipMalloc(&d, 2 * n)) != hipSuccess) return fail(EXQ_ERR_OOM, "hipMalloc expanded scales");
+    hipLaunchKernelGGL(expand_qs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(L->qscale), static_cast<const uint16_t*>(L->ref), L->d_meta, L->G,
+                       L->N, d);
+    if ((e = hipGetLastError()) != hipSuccess || (e = hipStreamSynchronize(stream)) != hipSuccess) {
+        (void)hipFree(d);
+        return hip_fail(e, "expanding the quantized scales");
+    }
+    L->d_scales_own.store(d, std::memory_order_release);
+    return EXQ_OK;
+}
+
 namespace {
 
 // exq_gemm with a given kernel choice (kVarDefault: M <= kTuneMaxM decode in
 // 16-row slices with the tile_cols_for width, else prefill: a 256-row prefill
 // tile mostly empty is slower than a few decode slices, measured 3x at 32
 // rows on every 70B shape).
-exq_status run_variant(const exq_layer* L, const void* x, int M, void* y, hipStream_t s, int v) {
+exq_status prefill_with_scales(exq_layer* L, const void* x, int M, void* y, hipStream_t s) {
+    exq_status st = ensure_scales(L, s);
+    return st != EXQ_OK ? st : exq_prefill_launch(L, x, M, y, s);
+}
+
+exq_status run_variant(exq_layer* L, const void* x, int M, void* y, hipStream_t s, int v) {
     switch (v) {
         case kVarDecode16: return exq_decode_rows(L, x, M, y, s, 16);
         case kVarDecode64: return exq_decode_rows(L, x, M, y, s, 64);
-        case kVarPrefill: return exq_prefill_launch(L, x, M, y, s);
-        default: return M > kTuneMaxM ? exq_prefill_launch(L, x, M, y, s) : exq_decode_rows(L, x, M, y, s);
+        case kVarPrefill: return prefill_with_scales(L, x, M, y, s);
+        default: return M > kTuneMaxM ? prefill_with_scales(L, x, M, y, s) : exq_decode_rows(L, x, M, y, s);
     }
 }
 
@@ -572,16 +671,20 @@ exq_status run_variant(const exq_layer* L, const void* x, int M, void* y, hipStr
 
 extern "C" {
 
-exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_host,
-                            const void* d_qweight, const void* d_scales, exq_layer_t* out) {
+// Shared by exq_layer_create (d_scales given) and exq_layer_create_qs
+// (d_qscale and d_ref given; the fp16 expansion is allocated and filled here).
+static exq_status layer_create(int K, int N, int group_size, const uint8_t* widths_host, const void* d_qweight,
+                               const void* d_scales, const void* d_qscale, const void* d_ref, exq_layer_t* out) {
     if (!out) return fail(EXQ_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     exq_status st = check_layer_shape(K, N, group_size, widths_host);
     if (st != EXQ_OK) return st;
     if (N % 64) return fail(EXQ_ERR_INVALID_ARG, "N=%d is not a multiple of 64", N);
-    if (!d_qweight || !d_scales) return fail(EXQ_ERR_INVALID_ARG, "NULL device buffer");
-    if (!aligned16(d_qweight) || !aligned16(d_scales))
-        return fail(EXQ_ERR_INVALID_ARG, "qweight and scales must be 16-byte aligned");
+    const bool qs = d_scales == nullptr;
+    if (!d_qweight || (!qs && !d_scales) || (qs && (!d_qscale || !d_ref)))
+        return fail(EXQ_ERR_INVALID_ARG, "NULL device buffer");
+    if (!aligned16(d_qweight) || (!qs && !aligned16(d_scales)) || (qs && (!aligned16(d_qscale) || !aligned16(d_ref))))
+        return fail(EXQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
     const int G = K / kGroup;
     {
         size_t words = 0;
@@ -600,6 +703,9 @@ exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_
     L->widths.assign(widths_host, widths_host + G);
     L->qweight = d_qweight;
     L->scales = d_scales;
+    L->qs = qs;
+    L->qscale = d_qscale;
+    L->ref = d_ref;
     L->plan = plan_waves(K, widths_host);
     std::vector<uint32_t> meta = group_meta(K, widths_host);
     hipError_t e = hipSuccess;
@@ -620,12 +726,31 @@ exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_
     return EXQ_OK;
 }
 
+exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_host, const void* d_qweight,
+                            const void* d_scales, exq_layer_t* out) {
+    if (!d_scales) {
+        if (out) *out = nullptr;
+        return fail(EXQ_ERR_INVALID_ARG, "NULL device buffer");
+    }
+    return layer_create(K, N, group_size, widths_host, d_qweight, d_scales, nullptr, nullptr, out);
+}
+
+exq_status exq_layer_create_qs(int K, int N, int group_size, const uint8_t* widths_host, const void* d_qweight,
+                               const void* d_qscale, const void* d_ref, exq_layer_t* out) {
+    if (!d_qscale || !d_ref) {
+        if (out) *out = nullptr;
+        return fail(EXQ_ERR_INVALID_ARG, "NULL device buffer");
+    }
+    return layer_create(K, N, group_size, widths_host, d_qweight, nullptr, d_qscale, d_ref, out);
+}
+
 void exq_layer_destroy(exq_layer_t L) {
     if (!L) return;
     if (L->d_meta) (void)hipFree(L->d_meta);
     if (L->d_order) (void)hipFree(L->d_order);
     if (L->d_bounds) (void)hipFree(L->d_bounds);
     if (L->d_runs) (void)hipFree(L->d_runs);
+    if (uint16_t* s = L->d_scales_own.load()) (void)hipFree(s);
     delete L;
 }
 
@@ -717,13 +842,16 @@ exq_status exq_gemm_gated(const void* x, int M, exq_layer_t gate, exq_layer_t up
     if (gate->K != up->K || gate->N != up->N)
         return fail(EXQ_ERR_INVALID_ARG, "gate (K=%d, N=%d) and up (K=%d, N=%d) differ in shape", gate->K, gate->N,
                     up->K, up->N);
+    if (gate->qs != up->qs) return fail(EXQ_ERR_INVALID_ARG, "gate and up differ in scale storage");
     if (!aligned16(x) || !aligned16(h)) return fail(EXQ_ERR_INVALID_ARG, "x and h must be 16-byte aligned");
     if (overlap(x, 2 * (size_t)M * gate->K, h, 2 * (size_t)M * gate->N))
         return fail(EXQ_ERR_INVALID_ARG, "h overlaps x");
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (M > kTuneMaxM) {
         // Gate product into h, then the up product's epilogue combines in place.
-        exq_status st = exq_prefill_launch(gate, x, M, h, s);
+        exq_status st = ensure_scales(gate, s);
+        if (st == EXQ_OK) st = ensure_scales(up, s);
+        if (st == EXQ_OK) st = exq_prefill_launch(gate, x, M, h, s);
         return st != EXQ_OK ? st : exq_prefill_launch_gated(up, x, M, h, s);
     }
     // Decode in 16-row slices; the tile width follows exq_gemm's rule.  (16-
@@ -746,6 +874,8 @@ exq_status exq_dequant(exq_layer_t L, void* w_out, void* stream) {
     if (!L) return fail(EXQ_ERR_INVALID_ARG, "layer is NULL");
     if (!w_out) return fail(EXQ_ERR_INVALID_ARG, "w_out is NULL");
     if (!aligned16(w_out)) return fail(EXQ_ERR_INVALID_ARG, "w_out must be 16-byte aligned");
+    exq_status st = ensure_scales(L, static_cast<hipStream_t>(stream));
+    if (st != EXQ_OK) return st;
     LinearDev d = linear_dev(L, nullptr, nullptr);
     hipLaunchKernelGGL(dequant_kernel, dim3(L->N / kTileCols, L->G), dim3(64), 0, static_cast<hipStream_t>(stream), d,
                        static_cast<uint16_t*>(w_out));
@@ -787,7 +917,13 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
             if (j != i && overlap(ys[i], 2 * (size_t)M * L->N, ys[j], 2 * (size_t)M * layers[j]->N))
                 return fail(EXQ_ERR_INVALID_ARG, "outputs %d and %d overlap", i, j);
         }
+        if (prefill) {
+            exq_status st = ensure_scales(layers[i], nullptr);
+            if (st != EXQ_OK) return st;
+        }
         list[i] = linear_dev(L, xs[i], const_cast<void*>(ys[i]));
+        if (!prefill && L->qs != layers[0]->qs)
+            return fail(EXQ_ERR_INVALID_ARG, "a decode plan needs one scale storage for all linears (entry %d differs)", i);
         if (prefill) {
             list[i].tiles = exq_prefill_tiles(L, M);
             if (list[i].tiles == 0) return fail(EXQ_ERR_UNSUPPORTED, "entry %d: K or M too large for a prefill plan", i);
@@ -838,6 +974,7 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
     P->count = count;
     P->M = M;
     P->prefill = prefill;
+    P->qs = !prefill && layers[0]->qs;
     P->total_wgs = (int)wg_map.size();
     hipError_t e;
     if ((e = hipMalloc(&P->d_list, sizeof(LinearDev) * count)) != hipSuccess ||

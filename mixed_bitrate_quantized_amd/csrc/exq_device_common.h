@@ -30,6 +30,10 @@ struct LinearDev {
     int K, N, G, tiles;
     uint32_t qbytes;          // bytes of qweight (< 2^31)
     uint32_t sbytes;          // bytes of scales
+    const uint8_t* qscale;    // quantized scales: 4-bit codes [G][N/2] (else null)
+    const uint16_t* ref;      // quantized scales: fp16 column range references [N]
+    uint32_t qsbytes;         // bytes of qscale
+    int qs;                   // 1: decode reads qscale/ref (scales holds their expansion)
 };
 
 // Weights and scales are read with raw buffer loads.  A load whose offset is

@@ -144,6 +144,33 @@ WavePlan plan_waves(int K, const uint8_t* widths) {
     return p;
 }
 
+// --------------------------------------------------- quantized group scales
+
+// fp16 scale of 4-bit scale code q at width b under column range reference R:
+// t = R (q+1)^2 / 256 is exact in fp32; one fp32 product with the fp32
+// reciprocal of 2^(b-1)-1, then fp16 round to nearest even.
+static uint16_t qs_scale_bits(float R, int q, int b) {
+    const float t = R * (float)((q + 1) * (q + 1)) * 0.00390625f;
+    const float inv = 1.0f / (float)((1 << (b - 1)) - 1);
+    return f32_to_f16(t * inv);
+}
+
+// Codes of one column's group at scale s16 (the exq_pack rule) and their
+// squared error sum_i (w_i - w_hat_i)^2, accumulated in double in index order.
+static double codes_at_scale(const float* w, int b, uint16_t s16, uint8_t* codes) {
+    const int z = 1 << (b - 1), qmax = z - 1;
+    const float s = f16_to_f32(s16);
+    double e = 0.0;
+    for (int i = 0; i < kGroup; ++i) {
+        float q = 0.0f;
+        if (s != 0.0f) q = std::min(std::max(std::nearbyint(w[i] / s), (float)-qmax), (float)qmax);
+        codes[i] = (uint8_t)((int)q + z);
+        const double d = (double)w[i] - (double)f16_to_f32(f32_to_f16(q * s));
+        e += d * d;
+    }
+    return e;
+}
+
 // ------------------------------------------------------- width allocation
 
 constexpr int kNumOpts = 6;
@@ -204,6 +231,71 @@ size_t exq_packed_bytes(int K, int N, int group_size, const uint8_t* widths) {
     size_t total = 0;
     for (int g = 0; g < K / kGroup; ++g) total += (size_t)widths[g] * kGroup * (size_t)N / 8;
     return total;
+}
+
+exq_status exq_pack_qs(const float* W, int K, int N, int group_size, const uint8_t* widths, void* qweight_out,
+                       uint8_t* qscale_out, uint16_t* ref_out) {
+    exq_status st = check_layer_shape(K, N, group_size, widths);
+    if (st != EXQ_OK) return st;
+    if (!W || !qweight_out || !qscale_out || !ref_out) return fail(EXQ_ERR_INVALID_ARG, "NULL buffer");
+    if (N % 2) return fail(EXQ_ERR_INVALID_ARG, "N=%d must be even for 4-bit scale codes", N);
+    const int G = K / kGroup;
+    std::vector<uint64_t> P(G + 1, 0);
+    for (int g = 0; g < G; ++g) P[g + 1] = P[g] + widths[g];
+    std::vector<uint8_t> qcode((size_t)G * N);
+    uint8_t* qw = static_cast<uint8_t*>(qweight_out);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+    for (int n = 0; n < N; ++n) {
+        const float* row = W + (size_t)n * K;
+        float range = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const float a = std::fabs(row[k]);
+            if (!(a <= 3.4e38f)) bad |= 1;
+            range = std::max(range, a);
+        }
+        const uint16_t r16 = f32_to_f16(range);
+        if ((r16 & 0x7C00u) == 0x7C00u) bad |= 2;
+        if (bad) continue;
+        ref_out[n] = r16;
+        const float R = f16_to_f32(r16);
+        uint8_t codes[kGroup], alt[kGroup];
+        uint32_t dw[32];
+        for (int g = 0; g < G; ++g) {
+            const int b = widths[g];
+            const float* w = row + (size_t)g * kGroup;
+            float amax = 0.0f;
+            for (int i = 0; i < kGroup; ++i) amax = std::max(amax, std::fabs(w[i]));
+            // the smallest code whose scale covers the group's range, then one
+            // code lower if that quantizes the group with less squared error
+            int q = 0;
+            if (R != 0.0f) {
+                const float c = std::ceil(16.0f * std::sqrt(amax / R));
+                q = (c < 1.0f ? 1 : (c > 16.0f ? 16 : (int)c)) - 1;
+            }
+            uint16_t s16 = qs_scale_bits(R, q, b);
+            const double e = codes_at_scale(w, b, s16, codes);
+            if (q >= 1) {
+                const uint16_t lower = qs_scale_bits(R, q - 1, b);
+                if (codes_at_scale(w, b, lower, alt) < e) {
+                    --q;
+                    s16 = lower;
+                    std::memcpy(codes, alt, kGroup);
+                }
+            }
+            qcode[(size_t)g * N + n] = (uint8_t)q;
+            pack_column_group(codes, b, dw);
+            uint8_t* base = qw + 16 * ((size_t)N * P[g] + (size_t)n);
+            for (int j = 0; j < b; ++j) std::memcpy(base + 16 * (size_t)j * N, dw + 4 * j, 16);
+        }
+    }
+    if (bad & 1) return fail(EXQ_ERR_INVALID_ARG, "W holds a NaN or infinity");
+    if (bad & 2) return fail(EXQ_ERR_INVALID_ARG, "a column range overflows fp16 (|w| too large)");
+    for (int g = 0; g < G; ++g)
+        for (int n = 0; n < N; n += 2)
+            qscale_out[(size_t)g * (N / 2) + n / 2] =
+                (uint8_t)(qcode[(size_t)g * N + n] | (qcode[(size_t)g * N + n + 1] << 4));
+    return EXQ_OK;
 }
 
 exq_status exq_pack(const float* W, int K, int N, int group_size, const uint8_t* widths,

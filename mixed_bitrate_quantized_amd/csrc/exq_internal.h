@@ -3,6 +3,7 @@
 
 #include <atomic>
 #include <cstddef>
+#include <mutex>
 #include <cstdint>
 #include <vector>
 
@@ -55,7 +56,14 @@ struct exq_layer {
     int K, N, G;
     std::vector<uint8_t> widths;
     const void* qweight;      // borrowed
-    const void* scales;       // borrowed
+    const void* scales;       // borrowed fp16 [G][N]; for quantized scales the owned expansion, once made
+    bool qs = false;          // quantized group scales (4-bit codes + column references)
+    const void* qscale = nullptr;     // borrowed 4-bit codes [G][N/2]
+    const void* ref = nullptr;        // borrowed fp16 [N]
+    // fp16 expansion of the quantized scales for the prefill and dequant
+    // kernels, made on the first call that needs it (ensure_scales).
+    std::atomic<uint16_t*> d_scales_own{nullptr};
+    std::mutex expand_mu;
     exq::WavePlan plan;
     uint32_t* d_meta = nullptr;
     uint32_t* d_order = nullptr;

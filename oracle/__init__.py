@@ -62,6 +62,7 @@ def _load():
     lib.oracle_pack.argtypes = [vp, i32, i32, vp, vp]
     lib.oracle_unpack.argtypes = [vp, i32, i32, vp, vp]
     lib.oracle_quantize.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.oracle_quantize_qs.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
     lib.oracle_dequant.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.oracle_gemm.argtypes = [vp, i32, vp, i32, i32, vp, vp]
     lib.oracle_gemm.restype = None
@@ -116,6 +117,22 @@ def quantize(W: np.ndarray, widths):
     scales = np.empty((K // GROUP, N), dtype=np.uint16)
     _check(_load().oracle_quantize(_p(W), K, N, _p(w), _p(codes), _p(scales)), "quantize")
     return codes, scales
+
+
+def quantize_qs(W: np.ndarray, widths):
+    """Quantized group scales: (codes uint8 [N][K], column range reference R fp16 bits [N],
+    qscale bytes [G][N/2], expanded scales fp16 bits [G][N]) from W fp32 [N][K] (see exq_oracle.c)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    w = _c(widths, np.uint8)
+    G = K // GROUP
+    codes = np.empty((N, K), dtype=np.uint8)
+    ref = np.empty(N, dtype=np.uint16)
+    qscale = np.zeros((G, N // 2), dtype=np.uint8)
+    scales = np.empty((G, N), dtype=np.uint16)
+    _check(_load().oracle_quantize_qs(_p(W), K, N, _p(w), _p(codes), _p(ref), _p(qscale), _p(scales)),
+           "quantize_qs")
+    return codes, ref, qscale, scales
 
 
 def pack(codes: np.ndarray, widths) -> np.ndarray:

@@ -240,6 +240,119 @@ int oracle_quantize(const float* W, int K, int N, const uint8_t* widths, uint8_t
     return 0;
 }
 
+/* Codes of one column's group at fp16 scale s16 (the rule of
+ * oracle_quantize); returns sum_i (w_i - w_hat_i)^2 in double, i ascending,
+ * w_hat = fp16_RNE((c - z) * s). */
+static double quantize_group_at(const float* w, int b, uint16_t s16, uint8_t* c) {
+    int z = 1 << (b - 1), qmax = z - 1;
+    float s = (float)oracle_f16_to_double(s16);
+    double err = 0.0;
+    for (int i = 0; i < ORACLE_GROUP; ++i) {
+        int q = 0;
+        if (s != 0.0f) {
+            volatile float r = w[i] / s;
+            float qq = nearbyintf(r);
+            if (qq > (float)qmax) qq = (float)qmax;
+            if (qq < (float)-qmax) qq = (float)-qmax;
+            q = (int)qq;
+        }
+        c[i] = (uint8_t)(q + z);
+        double wh = oracle_f16_to_double(oracle_f16_from_double((double)q * (double)s));
+        double d = (double)w[i] - wh;
+        err += d * d;
+    }
+    return err;
+}
+
+/* The fp16 scale of 4-bit scale code q under column reference R at width b:
+ * fp16_RNE(fp32(t * fp32(1 / (2^(b-1)-1)))) with t = R (q+1)^2 / 256 (exact). */
+static uint16_t qs_scale(float R, int q, int b) {
+    volatile float t = R * (float)((q + 1) * (q + 1)) * 0.00390625f;
+    volatile float inv = 1.0f / (float)((1 << (b - 1)) - 1);
+    volatile float u = t * inv;
+    return oracle_f16_from_double((double)u);
+}
+
+/* Quantized group scales: a 4-bit code per (group, column) relative to a
+ * per-column reference, on a square-root scale (the exllamav2 report's 4-bit
+ * second-level scale code, section "innovations", with a scan of candidate
+ * scales by their error; the formula printed there is garbled, so this is
+ * our specification).  The coded quantity is the group's range max|w|,
+ * which does not depend on its width:
+ *   amax[g][n] = max |w| over the group (fp32)
+ *   R[n]       = fp16_RNE(max_g amax[g][n])
+ *   qc[g][n]   = clamp(ceil(16 * sqrtf(amax / fp32(R))), 1, 16) - 1, in fp32
+ *                (IEEE division and square root): the smallest code whose
+ *                scale covers the range; 0 if R == 0
+ *   scale(q)   = fp16_RNE(fp32(t * fp32(1 / (2^(b-1) - 1)))), t = fp32(R)(q+1)^2/256
+ *   q[g][n]    = qc, or qc - 1 if that gives a strictly smaller squared error
+ *                sum_i (w_i - w_hat_i)^2 (double, i ascending; qc >= 1)
+ * with codes by the rule of oracle_quantize at scale(q).  Storage: R fp16 [N];
+ * qscale bytes [G][N/2], byte g*(N/2) + n/2 holding q of column n in its low
+ * nibble for even n and its high nibble for odd n.  scales_out receives the
+ * expanded scale(q) [G][N].  N must be even.  Returns 2 if R is not a finite
+ * fp16. */
+int oracle_quantize_qs(const float* W, int K, int N, const uint8_t* widths, uint8_t* codes, uint16_t* ref_out,
+                       uint8_t* qscale, uint16_t* scales_out) {
+    if (K % ORACLE_GROUP || N % 2) return 1;
+    int G = K / ORACLE_GROUP;
+    for (int g = 0; g < G; ++g)
+        if (!width_ok(widths[g])) return 1;
+    int overflow = 0;
+    uint8_t* qcode = (uint8_t*)malloc((size_t)G * N);   /* q[g][n], packed into nibbles at the end */
+    if (!qcode) return 3;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int n = 0; n < N; ++n) {
+        float mx = 0.0f;
+        for (int g = 0; g < G; ++g)
+            for (int i = 0; i < ORACLE_GROUP; ++i) {
+                float a = fabsf(W[(size_t)n * K + (size_t)g * ORACLE_GROUP + i]);
+                if (a > mx) mx = a;
+            }
+        uint16_t r16 = oracle_f16_from_double((double)mx);
+        if ((r16 & 0x7C00u) == 0x7C00u) { overflow = 1; continue; }
+        ref_out[n] = r16;
+        float R = (float)oracle_f16_to_double(r16);
+        uint8_t alt[ORACLE_GROUP];
+        for (int g = 0; g < G; ++g) {
+            int b = widths[g];
+            const float* w = W + (size_t)n * K + (size_t)g * ORACLE_GROUP;
+            uint8_t* c = codes + (size_t)n * K + (size_t)g * ORACLE_GROUP;
+            float amax = 0.0f;
+            for (int i = 0; i < ORACLE_GROUP; ++i) {
+                float a = fabsf(w[i]);
+                if (a > amax) amax = a;
+            }
+            int q = 0;
+            if (R != 0.0f) {
+                volatile float ratio = amax / R;
+                volatile float root = sqrtf(ratio);
+                float t = ceilf(16.0f * root);
+                q = (t < 1.0f ? 1 : (t > 16.0f ? 16 : (int)t)) - 1;
+            }
+            uint16_t s16 = qs_scale(R, q, b);
+            double e = quantize_group_at(w, b, s16, c);
+            if (q >= 1) {
+                uint16_t s16b = qs_scale(R, q - 1, b);
+                double eb = quantize_group_at(w, b, s16b, alt);
+                if (eb < e) {
+                    q -= 1;
+                    s16 = s16b;
+                    memcpy(c, alt, ORACLE_GROUP);
+                }
+            }
+            qcode[(size_t)g * N + n] = (uint8_t)q;
+            scales_out[(size_t)g * N + n] = s16;
+        }
+    }
+    for (int g = 0; g < G && !overflow; ++g)
+        for (int n = 0; n < N; n += 2)
+            qscale[(size_t)g * (N / 2) + n / 2] =
+                (uint8_t)(qcode[(size_t)g * N + n] | (qcode[(size_t)g * N + n + 1] << 4));
+    free(qcode);
+    return overflow ? 2 : 0;
+}
+
 /* ---------------------------------------------------------------- dequant */
 
 /* w_hat fp16 bits [K][N] row-major from codes [N][K] and scales [G][N]. */

@@ -14,9 +14,12 @@
 //     kernel reads -- and decodes it itself, into its own A operands, with
 //     wave-uniform shifts and register picks.  W_hat never goes through LDS
 //     and no dequantized value is computed twice;
-//   * x is staged in LDS, [256 rows][64 k] per stage, double-buffered, rows
-//     padded to 72 halves so that 16-byte operand reads of 8 or 16
-//     consecutive rows fall in distinct banks; one barrier per stage;
+//   * x is copied from global memory straight into LDS (buffer loads with
+//     the LDS flag: no registers, no LDS store instructions), [256 rows]
+//     [64 k] per stage, 4 buffers so that a stage's copy has two stages to
+//     land; 16-byte chunks are XOR-swizzled within a row so that operand
+//     reads of 16 consecutive rows fall in distinct banks; one barrier per
+//     stage;
 //   * decoding is exact and width-generic: a code goes into the low byte of
 //     an fp16 whose high byte is 0x64, which reads 1024 + c; one packed
 //     subtract of 1024 + z and one packed multiply by the scale give
@@ -36,7 +39,7 @@ namespace {
 
 constexpr int kPT = 256;        // tile rows of x and tile columns of W
 constexpr int kPK = 64;         // K per stage: half a group
-constexpr int kPLd = kPK + 8;   // padded LDS row length of the x tile, halves
+constexpr int kPXBytes = kPT * kPK * 2;   // one stage's x tile in LDS: 256 rows of 128 bytes
 constexpr int kPThreads = 256;  // 4 waves
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -47,22 +50,35 @@ struct PrefillCtx {
     int tid, lane, wave;
     uint32_t q;        // K-quarter of the half group this lane decodes (lane / 32)
     uint32_t col[2];   // its two columns (clamped into [0, N): extra columns are never stored)
+    uint32_t xo[4];    // LDS byte offset of the lane's x operand of K-step kk in row block 0
+    uint32_t xv[8];    // x buffer offset of the 16 bytes the lane copies in copy `it` of a stage
 };
+
+// x tile rows are 128 bytes (8 slots of 16 bytes); k chunk kc of row r sits in
+// slot kc ^ xswz(r), so that 16-byte operand reads of 16 consecutive rows at
+// one kc touch 16 distinct slot / row-parity pairs: no bank conflicts.
+__device__ __forceinline__ uint32_t xswz(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
 
 // Where stage st comes from: half h = st % 2 of group g = st / 2.  A stage
 // past the last one reloads the last (cache hits, never used): a uniform test
-// on it would split the stage into branches.
+// on it would split the stage into branches.  Stages -2 and -1 (run first
+// when the stage count is 2 mod 4) read stage 0's words with an out-of-range
+// scale offset: scale 0, so every weight they decode is a zero.
 struct StageSrc {
-    uint32_t g, P, h;
+    uint32_t g, P, h, so;   // so: byte offset of the group's scales (out of range: zeros)
     int b;
 };
 
 __device__ __forceinline__ StageSrc stage_src(const LinearDev& L, int st, int S) {
-    st = min(st, S - 1);
+    const uint32_t null_scale = st < 0 ? kBufOOB : 0u;
+    st = max(min(st, S - 1), 0);
     StageSrc r;
     r.g = (uint32_t)(st >> 1);
     r.h = (uint32_t)(st & 1);
-    const uint32_t meta = gptr<uint32_t>(L.meta)[r.g];
+    r.so = null_scale + 2u * r.g * (uint32_t)L.N;
+    // Read-only for the kernel: a constant-space load keeps it scalar although
+    // the LDS copies count as memory writes.
+    const uint32_t meta = ((const __attribute__((address_space(4))) uint32_t*)L.meta)[r.g];
     r.P = meta >> 4;
     r.b = (int)(meta & 15u);
     return r;
@@ -89,36 +105,35 @@ __device__ __forceinline__ void issue_w(const LinearDev& L, const PrefillCtx& c,
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const uint32_t base = 16u * ((uint32_t)L.N * src.P + c.col[i]);
-        const u2v a0 = __builtin_amdgcn_raw_buffer_load_b64(c.rw, base + offA, 0, 0);
-        const u2v a1 = __builtin_amdgcn_raw_buffer_load_b64(c.rw, p0 >= 4 ? base + offA + 8u : kBufOOB, 0, 0);
+        const u4v a = __builtin_amdgcn_raw_buffer_load_b128(c.rw, base + offA, 0, 0);
         const u4v bq = __builtin_amdgcn_raw_buffer_load_b128(c.rw, p0 == 8 ? base + offA + N16 : kBufOOB, 0, 0);
-        const uint32_t h0 = __builtin_amdgcn_raw_buffer_load_b32(c.rw, p1 >= 1 ? base + offC : kBufOOB, 0, 0);
-        const uint32_t h1 = __builtin_amdgcn_raw_buffer_load_b32(c.rw, p1 == 2 ? base + offC + 4u : kBufOOB, 0, 0);
-        W[i].q[0] = a0[0];
-        W[i].q[1] = a0[1];
-        W[i].q[2] = a1[0];
-        W[i].q[3] = a1[1];
+        const u2v hh = __builtin_amdgcn_raw_buffer_load_b64(c.rw, p1 >= 1 ? base + offC : kBufOOB, 0, 0);
+        W[i].q[0] = a[0];
+        W[i].q[1] = a[1];
+        W[i].q[2] = a[2];
+        W[i].q[3] = a[3];
         W[i].q[4] = bq[0];
         W[i].q[5] = bq[1];
         W[i].q[6] = bq[2];
         W[i].q[7] = bq[3];
-        W[i].h[0] = h0;
-        W[i].h[1] = h1;
+        W[i].h[0] = hh[0];
+        W[i].h[1] = hh[1];
         W[i].s = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
-            c.rs, 2u * (src.g * (uint32_t)L.N + c.col[i]), 0, 0);
+            c.rs, src.so + 2u * c.col[i], 0, 0);
     }
 }
 
-// x chunk `it` of a stage: row it * 32 + tid / 8 of the tile, k chunk tid % 8.
-// Rows past M are outside the x buffer: zeros.
-__device__ __forceinline__ u4v issue_x(const LinearDev& L, const PrefillCtx& c, const StageSrc& src, int it) {
-    const uint32_t r = (uint32_t)(it * 32 + (c.tid >> 3)), kc = (uint32_t)(c.tid & 7);
-    const uint32_t off = 2u * (r * (uint32_t)L.K + 128u * src.g + 64u * src.h + 8u * kc);
-    return __builtin_amdgcn_raw_buffer_load_b128(c.rx, off, 0, 0);
-}
-
-__device__ __forceinline__ void store_x_chunk(const u4v& v, uint16_t* sx, int tid, int it) {
-    *reinterpret_cast<u4v*>(sx + (it * 32 + (tid >> 3)) * kPLd + 8 * (tid & 7)) = v;
+// Copy `it` of a stage: the wave's 64 lanes move rows 64 w + 8 it .. + 8 of
+// the stage's x tile (1 KiB) straight into LDS, lane i writing bytes
+// [16 i, 16 i + 16) of that KiB, so lane i fetches k chunk
+// (i % 8) ^ xswz(row) of row 64 w + 8 it + i / 8.  The stage's position in K
+// goes in the scalar offset; rows past M fail the range check of the
+// vector offset and read zeros.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ void copy_x(const PrefillCtx& c, const StageSrc& src, uint16_t* sx, int it) {
+    const uint32_t soff = 256u * src.g + 128u * src.h;
+    char* dst = reinterpret_cast<char*>(sx) + 1024 * (8 * c.wave + it);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (lds_ptr_t)dst, 16, (int)c.xv[it], (int)soff, 0, 0);
 }
 
 // Width-generic decoding.  For unit U (codes 4U .. 4U+3 of a K-quarter) the
@@ -214,9 +229,9 @@ struct Ops {
 // x operand of K-step kk: lane l holds row 32 jb + l % 32 of the tile and the
 // x values that meet its k-slots, k = 32 (l / 32) + 8 kk + [0, 8).
 __device__ __forceinline__ void load_x_ops(const uint16_t* sx, const PrefillCtx& c, int kk, Ops& o) {
-    const int off = (c.lane & 31) * kPLd + 32 * (c.lane >> 5) + 8 * kk;
+    const char* base = reinterpret_cast<const char*>(sx) + c.xo[kk];
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb) o.x[jb] = *reinterpret_cast<const h8*>(sx + jb * 32 * kPLd + off);
+    for (int jb = 0; jb < 8; ++jb) o.x[jb] = *reinterpret_cast<const h8*>(base + jb * 32 * 128);
 }
 
 __device__ __forceinline__ void mfma_ops(const Ops& o, f16v (&acc)[2][8]) {
@@ -240,14 +255,14 @@ __device__ __forceinline__ void region_schedule() {
 }
 
 // Stage st.  On entry LDS buffer rd_x holds stage st's x tile, Wc its packed
-// words, xr stage st+1's x chunks, `carry` the operands of the previous
-// stage's last K-step.  Region r reads and decodes the operands of K-step r
-// and multiplies K-step r - 1 (region 0: `carry`, prepared before the
-// barrier), so no MFMA waits for work issued in its own region; it also
-// moves two x chunks of stage st+1 into wr_x and loads those of stage st+2.
-// Stage st+1's packed words go into Wn.  sched_barrier keeps the regions
-// apart so the scheduler interleaves within a region without hoisting a
-// whole stage's operands.
+// words, `carry` the operands of the previous stage's last K-step; stage
+// st + 1's x tile is landing in another buffer.  Region r reads and decodes
+// the operands of K-step r and multiplies K-step r - 1 (region 0: `carry`,
+// prepared before the barrier), so no MFMA waits for work issued in its own
+// region; it also starts two of the wave's copies of stage st + 2's x tile
+// into wr_x, the buffer stage st - 2 read.  Stage st+1's packed words go into
+// Wn.  sched_barrier keeps the regions apart so the scheduler interleaves
+// within a region without hoisting a whole stage's operands.
 //
 // The scalars of the next stage (src3: stage st+3, T_n: the width row of
 // stage st+1) are loaded at the very end and first used after the closing
@@ -255,9 +270,9 @@ __device__ __forceinline__ void region_schedule() {
 // while one is outstanding every wait for an operand read would drain all.
 __device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx& c, int st, int S,
                                            const uint16_t* rd_x, uint16_t* wr_x, const QRegs (&Wc)[2],
-                                           QRegs (&Wn)[2], u4v (&xr)[8], const StageSrc& src1,
-                                           const StageSrc& src2, const DqRow& T, StageSrc& src3, DqRow& T_n,
-                                           Ops& carry, Ops& other, f16v (&acc)[2][8]) {
+                                           QRegs (&Wn)[2], const StageSrc& src1, const StageSrc& src2,
+                                           const DqRow& T, StageSrc& src3, DqRow& T_n, Ops& carry, Ops& other,
+                                           f16v (&acc)[2][8]) {
     issue_w(L, c, src1, Wn);
     static_for<0, 4>([&](auto KC) {
         constexpr int KK = decltype(KC)::value;
@@ -266,10 +281,8 @@ __device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx&
         load_x_ops(rd_x, c, KK, rd);
         rd.a[0] = dequant_operand<KK>(Wc[0], T);
         rd.a[1] = dequant_operand<KK>(Wc[1], T);
-        store_x_chunk(xr[2 * KK], wr_x, c.tid, 2 * KK);
-        store_x_chunk(xr[2 * KK + 1], wr_x, c.tid, 2 * KK + 1);
-        xr[2 * KK] = issue_x(L, c, src2, 2 * KK);
-        xr[2 * KK + 1] = issue_x(L, c, src2, 2 * KK + 1);
+        copy_x(c, src2, wr_x, 2 * KK);
+        copy_x(c, src2, wr_x, 2 * KK + 1);
         mfma_ops(mul, acc);
         region_schedule();
         __builtin_amdgcn_sched_barrier(0);
@@ -277,6 +290,19 @@ __device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx&
     // Last, so that no wait inside the regions has a scalar load to cover.
     src3 = stage_src(L, st + 3, S);
     T_n = kDq[src1.b];
+}
+
+// Closes a stage.  A stage issues 16 vector memory operations (8 packed-word
+// loads, 8 copies), so waiting until at most 8 are outstanding completes
+// every one issued before it -- in particular the copies of the x tile the
+// next stage reads; then the barrier makes the copies of all waves visible.
+// The copies write LDS behind the compiler's back as far as __syncthreads is
+// concerned (its fence would wait for all of them), hence the explicit wait
+// and a bare barrier; sched_barrier keeps the next stage's reads below it.
+__device__ __forceinline__ void stage_end() {
+    __builtin_amdgcn_s_waitcnt((8 & 15) | ((8 >> 4) << 14) | (7 << 4) | (15 << 8));   // vmcnt(8)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // SiLU(g) * u in fp32 (g read back as fp16): g / (1 + e^-g) * u.
@@ -289,12 +315,12 @@ __device__ __forceinline__ float silu_mul_h(uint16_t g16, float u) {
 // y already holds the gate product g (fp16) of the same tile, and the tile
 // stores SiLU(g) * acc over it.
 template <bool GATED>
-__device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, int n0, uint16_t* sx0,
-                                             uint16_t* sx1) {
+__device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, int n0, uint16_t* sxa,
+                                             uint16_t* sxb, uint16_t* sxc, uint16_t* sxd) {
     PrefillCtx c;
     c.tid = threadIdx.x;
     c.lane = c.tid & 63;
-    c.wave = c.tid >> 6;
+    c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
     c.q = (uint32_t)(c.lane >> 5);
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) c.col[ib] = (uint32_t)min(n0 + 64 * c.wave + 32 * ib + (c.lane & 31), L.N - 1);
@@ -302,6 +328,17 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
     c.rs = buffer_rsrc(L.scales, L.sbytes);
     const int rows = min(M - m0, kPT);
     c.rx = buffer_rsrc(L.x + (size_t)m0 * L.K, 2u * (uint32_t)rows * (uint32_t)L.K);
+    {
+        // Operand reads: row lane % 32 of each row block, k chunk 4 (lane / 32) + kk.
+        const uint32_t r = (uint32_t)(c.lane & 31), s0 = (4u * c.q) ^ xswz(r);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) c.xo[kk] = 128u * r + 16u * (s0 ^ (uint32_t)kk);
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const uint32_t R = (uint32_t)(64 * c.wave + 8 * it + (c.lane >> 3));
+            c.xv[it] = 2u * (uint32_t)L.K * R + 16u * ((uint32_t)(c.lane & 7) ^ xswz(R));
+        }
+    }
 
     const int S = 2 * L.G;
     f16v acc[2][8];
@@ -313,23 +350,31 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
             for (int e = 0; e < 16; ++e) acc[ib][jb][e] = 0.f;
 
     QRegs W0[2], W1[2];
-    u4v xr[8];
     StageSrc s1, s2;
     DqRow T0;
+    // The loop runs 4 stages per trip, each with its own x buffer; a stage
+    // count of 2 mod 4 starts two stages early on zero x tiles and zero scales.
+    const int st0 = (S & 2) ? -2 : 0;
     {
-        // Stage 0's x tile is staged alone; from then on every stage stages the next.
-        const StageSrc s0 = stage_src(L, 0, S);
-        s1 = stage_src(L, 1, S);
-        s2 = stage_src(L, 2, S);
+        const StageSrc s0 = stage_src(L, st0, S);
+        s1 = stage_src(L, st0 + 1, S);
+        s2 = stage_src(L, st0 + 2, S);
         T0 = kDq[s0.b];
-        issue_w(L, c, s0, W0);
+        if (st0 == 0) {
 #pragma unroll
-        for (int it = 0; it < 8; ++it) xr[it] = issue_x(L, c, s0, it);
+            for (int it = 0; it < 8; ++it) copy_x(c, s0, sxa, it);
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            store_x_chunk(xr[it], sx0, c.tid, it);
-            xr[it] = issue_x(L, c, s1, it);
+            for (int it = 0; it < 8; ++it) copy_x(c, s1, sxb, it);
+        } else {
+            const u4v z = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < kPXBytes / 16 / kPThreads; ++k) {
+                *reinterpret_cast<u4v*>(reinterpret_cast<char*>(sxa) + 16 * (k * kPThreads + c.tid)) = z;
+                *reinterpret_cast<u4v*>(reinterpret_cast<char*>(sxb) + 16 * (k * kPThreads + c.tid)) = z;
+            }
         }
+        issue_w(L, c, s0, W0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
     // Zero operands: the first stage's region 0 adds exact zeros.
     Ops carry, other;
@@ -338,16 +383,20 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
     carry.a[0] = h8{};
     carry.a[1] = h8{};
     __syncthreads();
-    for (int st = 0; st < S; st += 2) {
-        StageSrc s3, s4;
-        DqRow T1, T2;
-        stage_body(L, c, st, S, sx0, sx1, W0, W1, xr, s1, s2, T0, s3, T1, carry, other, acc);
-        __syncthreads();
-        stage_body(L, c, st + 1, S, sx1, sx0, W1, W0, xr, s2, s3, T1, s4, T2, carry, other, acc);
-        __syncthreads();
-        s1 = s3;
-        s2 = s4;
-        T0 = T2;
+    for (int st = st0; st < S; st += 4) {
+        StageSrc s3, s4, s5, s6;
+        DqRow T1, T2, T3, T4;
+        stage_body(L, c, st, S, sxa, sxc, W0, W1, s1, s2, T0, s3, T1, carry, other, acc);
+        stage_end();
+        stage_body(L, c, st + 1, S, sxb, sxd, W1, W0, s2, s3, T1, s4, T2, carry, other, acc);
+        stage_end();
+        stage_body(L, c, st + 2, S, sxc, sxa, W0, W1, s3, s4, T2, s5, T3, carry, other, acc);
+        stage_end();
+        stage_body(L, c, st + 3, S, sxd, sxb, W1, W0, s4, s5, T3, s6, T4, carry, other, acc);
+        stage_end();
+        s1 = s5;
+        s2 = s6;
+        T0 = T4;
     }
     mfma_ops(carry, acc);
 
@@ -383,13 +432,15 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
 
 template <bool GATED>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, int row_tiles, int col_tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t sx0[kPT * kPLd];
-    __shared__ __attribute__((aligned(16))) uint16_t sx1[kPT * kPLd];
+    __shared__ __attribute__((aligned(1024))) uint16_t sxa[kPXBytes / 2];
+    __shared__ __attribute__((aligned(1024))) uint16_t sxb[kPXBytes / 2];
+    __shared__ __attribute__((aligned(1024))) uint16_t sxc[kPXBytes / 2];
+    __shared__ __attribute__((aligned(1024))) uint16_t sxd[kPXBytes / 2];
     // XCD-aware tile order: ids i, i+8, i+16, ... (one XCD) take consecutive tiles.
     const int T = row_tiles * col_tiles;
     const int i = blockIdx.x, xcd = i & 7, per = T >> 3, rem = T & 7;
     const int t = xcd * per + min(xcd, rem) + (i >> 3);
-    prefill_tile<GATED>(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sx0, sx1);
+    prefill_tile<GATED>(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sxa, sxb, sxc, sxd);
 }
 
 // Several linears in one launch: workgroup i takes entry i of wg_map
@@ -397,8 +448,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, 
 // host orders the map longest-K first and XCD-aware.
 __global__ __launch_bounds__(kPThreads) void prefill_plan_kernel(const LinearDev* __restrict__ list,
                                                                   const uint32_t* __restrict__ wg_map, int M) {
-    __shared__ __attribute__((aligned(16))) uint16_t sx0[kPT * kPLd];
-    __shared__ __attribute__((aligned(16))) uint16_t sx1[kPT * kPLd];
+    __shared__ __attribute__((aligned(1024))) uint16_t sxa[kPXBytes / 2];
+    __shared__ __attribute__((aligned(1024))) uint16_t sxb[kPXBytes / 2];
+    __shared__ __attribute__((aligned(1024))) uint16_t sxc[kPXBytes / 2];
+    __shared__ __attribute__((aligned(1024))) uint16_t sxd[kPXBytes / 2];
     const uint32_t e = gptr<uint32_t>(wg_map)[blockIdx.x];
     if (e == 0xFFFFFFFFu) return;   // padding entry: no tile
     LinearDev L;
@@ -411,7 +464,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_plan_kernel(const LinearDev
             dst[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)src[k]);   // uniform: SGPRs
     }
     const int col_tiles = (L.N + kPT - 1) / kPT, t = (int)(e >> 16);
-    prefill_tile<false>(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sx0, sx1);
+    prefill_tile<false>(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sxa, sxb, sxc, sxd);
 }
 
 }  // namespace

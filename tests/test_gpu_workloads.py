@@ -144,3 +144,42 @@ def test_cfg3_block_as_one_plan(exq, M):
     plan.close()
     for l in layers:
         l.close()
+
+
+def test_cfg4_block_as_one_plan(exq):
+    """The seven linears of a 70B-shaped block at M = 2048 as one prefill plan
+    (the launch bench.py times), each on a row and column sample against the
+    oracle, and the same bits on a second and third run."""
+    specs = workloads.linears(4)
+    M = workloads.M_VALUES[4][0]
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 32, replace=False)]))
+    layers, refs, xs_h = [], [], []
+    for spec in specs:
+        note("cfg4 plan %s: generate + pack" % spec.name)
+        W = workloads.make_weight(spec)
+        widths = workloads.make_widths(spec, W)
+        q, s = exq.exq_pack(W, widths)
+        codes, s_ref, q_ref = oracle.reference_layer(W, widths)
+        np.testing.assert_array_equal(s, s_ref)
+        np.testing.assert_array_equal(q, q_ref)
+        del W, codes
+        layers.append(exq.Layer(spec.K, spec.N, widths, q, s))
+        refs.append((q_ref, s_ref, widths, sample_cols(spec.N, 48, spec.w_seed() & 0xFFFF)))
+        xs_h.append(workloads.make_x(spec, M))
+    xs = [to_dev(x) for x in xs_h]
+    ys = [torch.empty((M, l.N), dtype=torch.float16, device="cuda") for l in layers]
+    note("cfg4 block plan M=%d" % M)
+    plan = exq.Plan(layers, xs, ys, M)
+    plan.run()
+    first = [y_to_np(y).copy() for y in ys]
+    for spec, x, g, (q, s, widths, cols) in zip(specs, xs_h, first, refs):
+        y_ref, bnd = oracle.gemm_packed_cols(x[rows], q, s, widths, spec.K, spec.N, cols)
+        assert_within(g[np.ix_(rows, cols)], y_ref, bnd, "cfg4 plan %s" % spec.name)
+    for _ in range(2):
+        plan.run()
+        for y, g in zip(ys, first):
+            np.testing.assert_array_equal(y_to_np(y), g)
+    plan.close()
+    for l in layers:
+        l.close()

@@ -10,9 +10,10 @@ Prints one JSON line: whole-step HBM throughput (algorithmic bytes / step
 time), ms/step, the decode kernel's roofline and the CPU oracle timed on a
 bounded sample of the same workload.  A second leg ("prefill") times the
 prefill path on the same seven 70B shapes at M = 2048 tokens (mixed 4.0 bpw
-from {3,4,5,6}) against the fp16 matrix-core peak.
+from {3,4,5,6}) against the fp16 matrix-core peak, and a third
+("batched_decode_m16") streams the same stack at M = 16 rows.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 5|3] [--m 1] [--no-prefill]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 5|3] [--m 1] [--no-prefill] [--no-batched]
 """
 from __future__ import annotations
 
@@ -267,6 +268,41 @@ def autotune_leg(exq, torch, layers, stream, Ms=(1, 4, 16, 32)):
     return out
 
 
+def batched_decode_leg(exq, torch, specs, layers, nblk, M, steps, stream):
+    """The same stack streamed per step at M rows (the batched-decode shape):
+    one decode plan per block, as in the headline step, on fresh x and y."""
+    from synth import workloads
+    xs = [torch.from_numpy(workloads.make_x(sp, M)).cuda() for sp in specs]
+    ys = [torch.empty((M, sp.N), dtype=torch.float16, device="cuda") for sp in specs]
+    per = len(specs) // nblk
+    plans = [exq.Plan(layers[b * per:(b + 1) * per], xs[b * per:(b + 1) * per], ys[b * per:(b + 1) * per], M)
+             for b in range(nblk)]
+    nbytes = sum(workloads.algorithmic_bytes(sp.K, sp.N, l.widths, M) for sp, l in zip(specs, layers))
+
+    def step():
+        for p in plans:
+            p.run(stream)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    for p in plans:
+        p.close()
+    del xs, ys
+    torch.cuda.empty_cache()
+    log("M=%d stack step %.3f ms, %.1f GB/s" % (M, ms, nbytes / (ms * 1e-3) / 1e9))
+    return {"workload": "the same %d-block stack at M=%d, one decode plan per block" % (nblk, M), "M": M,
+            "ms_per_step": round(ms, 4), "bytes_per_step": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2), "steps": steps}
+
+
 def gated_leg(exq, torch, layers, xs, M, nblk, steps, stream):
     """The 80 gate/up pairs of the stack: h = SiLU(x Wg^T) * (x Wu^T) per block
     as one exq_gemm_gated launch, against a two-linear plan plus torch's SiLU
@@ -396,6 +432,7 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=1, help="blocks of the workload the oracle is timed on")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum timed oracle work (the sample is repeated)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M = 2048 prefill leg")
+    ap.add_argument("--no-batched", action="store_true", help="skip the M = 16 pass over the stack")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--variants", action="store_true", help="also time per-linear calls, ungraphed and graphed")
     ap.add_argument("--no-stream-read", action="store_true", help="skip the plain streaming-read ceiling")
@@ -538,6 +575,10 @@ def main():
     if not args.no_gated and args.config == 5:
         gated = gated_leg(exq, torch, layers, xs, M, nblk, args.steps, stream)
 
+    batched = None
+    if not args.no_batched and args.config == 5 and M == 1:
+        batched = batched_decode_leg(exq, torch, specs, layers, nblk, 16, max(5, args.steps // 5), stream)
+
     traffic = None
     if os.path.exists(PROFILE_COUNTERS):
         with open(PROFILE_COUNTERS) as f:
@@ -654,6 +695,7 @@ def main():
         "step_stats": step_stats,
         "stream_read": read,
         "gated_gate_up": gated,
+        "batched_decode_m16": batched,
         "allocator": alloc,
         "autotune": tune,
         "quantized_scales": qsres,

@@ -34,6 +34,8 @@
 
 namespace exq {
 
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
 template <int B> __device__ constexpr float class_factor(int t) {
     // 2^(24 - o), o = p0 * t: turns c * 2^(o-24) back into c.
     return (float)(1u << (24 - Width<B>::p0 * t));
@@ -69,6 +71,7 @@ __device__ __forceinline__ void load_group_words(__amdgpu_buffer_rsrc_t rw, uint
 struct DecodeCtx {
     int M, lane, q, n;
     float ref;                       // quantized scales: the column's range reference R
+    float ref4[4];                   // the same for the four columns of a lane in the 16-row layout
     __amdgpu_buffer_rsrc_t rw, rs;   // weight and scale (or 4-bit scale code) buffers
 };
 
@@ -77,7 +80,7 @@ struct DecodeCtx {
 // or high (odd column) nibble, and s = fp16_RNE(fp32(t * fp32(1/(2^(b-1)-1))))
 // with t = R (q+1)^2 / 256, exact in fp32.
 template <int B, bool QS>
-__device__ __forceinline__ float group_scale(const DecodeCtx& c, uint16_t raw) {
+__device__ __forceinline__ float group_scale(float ref, int n, uint16_t raw) {
     if constexpr (!QS) {
         return (float)__builtin_bit_cast(_Float16, raw);
     } else {
@@ -86,8 +89,8 @@ __device__ __forceinline__ float group_scale(const DecodeCtx& c, uint16_t raw) {
         // without it the product and the conversion fuse into one
         // mixed-precision multiply (v_fma_mixlo_f16) that rounds once, to fp16.
         constexpr float inv = 1.0f / (float)((1 << (B - 1)) - 1);
-        const int q1 = (int)((raw >> (4 * (c.n & 1))) & 15u) + 1;
-        const float t = c.ref * (float)(q1 * q1) * 0.00390625f;
+        const int q1 = (int)((raw >> (4 * (n & 1))) & 15u) + 1;
+        const float t = ref * (float)(q1 * q1) * 0.00390625f;
         float u = t * inv;
         asm("" : "+v"(u));
         return (float)(_Float16)u;
@@ -161,7 +164,7 @@ __device__ __forceinline__ void group_compute(const DecodeCtx& c, const uint32_t
             acc[t][rb] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, acc[t][rb], TT::CBSZ, U >> 1, 0);
         }
     });
-    const float s = group_scale<B, QS>(c, s16);
+    const float s = group_scale<B, QS>(c.ref, c.n, s16);
     constexpr float z = (float)(1 << (B - 1));
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
@@ -179,6 +182,70 @@ __device__ __forceinline__ void group_compute(const DecodeCtx& c, const uint32_t
     }
 }
 
+// Which compute layout a (row blocks, tile width) pair uses, and the shape
+// of a lane's partial sums: [row block][row] for the 4x4x4 layout,
+// [column block][row] for the 16-row layout.
+template <int MB, int TC> struct Rows {
+    static constexpr bool MMA = TC == 64 && MB >= 2;
+    static constexpr int YB = MMA ? 4 : MB;
+    // Waves per SIMD the launch bounds ask for: the 16-row layout keeps two
+    // groups in flight per wave and fits 128 VGPRs, so two 8-wave workgroups
+    // share a CU (measured 1.2x faster than one with deeper pipelines).
+    static constexpr int WAVES_PER_EU = MMA ? 4 : 1;
+};
+
+// The 16-row layout (64-column tiles, M > 4).  Lane (j = l / 16, c = l % 16)
+// decodes K-quarter j of columns c, c + 16, c + 32, c + 48: exactly the B
+// operand of v_mfma_f32_16x16x32_f16 when MFMA k-slot 8j + t of K-step kk is
+// code 32j + 8kk + t of the group (units 2kk and 2kk + 1 of quarter j).  The
+// A operand is x in the same k order: lane (j, r) holds
+// x[r][128g + 32j + 8kk .. +8].  Lane (j, c) ends with rows 4j .. 4j + 3 of
+// its four columns.  Unit 2kk + 1 sits p0 bits above unit 2kk (the next
+// class); one shift puts both in unit 2kk's class, so each MFMA adds to one
+// class sum.  A fifth MFMA per K-step against all-z operands gives
+// z * sum_k x[r][k], the zero-point term, once for all columns.
+template <int B, bool QS>
+__device__ __forceinline__ void group_compute_mma(const DecodeCtx& c, const uint32_t (&Q)[4 * B], const u4v (&X)[4],
+                                                  const uint16_t (&S)[4], float (&yacc)[4][4]) {
+    using T = Width<B>;
+    constexpr int NCLS = T::per == 4 ? 2 : 1;   // classes 0 and 2 for 2- and 3-bit groups, else 0
+    f4 acc[4][NCLS], accz = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int k = 0; k < NCLS; ++k) acc[cb][k] = f4{0.f, 0.f, 0.f, 0.f};
+    constexpr uint32_t zh = (uint32_t)(15 + B - 1) << 10;   // fp16 bits of z = 2^(B-1)
+    const h8 zop = __builtin_bit_cast(h8, u4v{zh | (zh << 16), zh | (zh << 16), zh | (zh << 16), zh | (zh << 16)});
+    static_for<0, 4>([&](auto KC) {
+        constexpr int kk = decltype(KC)::value;
+        constexpr int cls = NCLS == 2 ? (kk & 1) : 0;
+        const h8 xop = __builtin_bit_cast(h8, X[kk]);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            uint32_t a0, a1, b0, b1;
+            unit_pair<B, 2 * kk, 1>(Q + cb * B, a0, a1);
+            unit_pair<B, 2 * kk + 1, 1>(Q + cb * B, b0, b1);
+            if constexpr (T::per >= 2) {
+                b0 >>= T::p0;
+                b1 >>= T::p0;
+            }
+            const h8 wop = __builtin_bit_cast(h8, u4v{a0, a1, b0, b1});
+            acc[cb][cls] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, wop, acc[cb][cls], 0, 0, 0);
+        }
+        accz = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, zop, accz, 0, 0, 0);
+    });
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const float s = group_scale<B, QS>(c.ref4[cb], c.n + 16 * cb, S[cb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float tv = acc[cb][0][i] * class_factor<B>(0);
+            if constexpr (NCLS == 2) tv = __builtin_fmaf(acc[cb][1][i], class_factor<B>(2), tv);
+            yacc[cb][i] = __builtin_fmaf(s, tv - accz[i], yacc[cb][i]);
+        }
+    }
+}
+
 template <int B, int TC> struct Depth {
     // groups in flight per wave (the one being computed included)
     static constexpr int value = TC == 64 ? ((B <= 2) ? 4 : (B <= 4 ? 3 : 2)) : ((B <= 3) ? 6 : (B <= 6 ? 4 : 3));
@@ -192,30 +259,45 @@ template <int B, int TC> struct Depth {
 // keep the count fixed, return zeros and cost no memory traffic.
 template <int B, int MB, int TC, bool M1, bool QS>
 __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c, const uint32_t* ord, int cnt,
-                                          float (&yacc)[MB][4]) {
-    constexpr int DEPTH = Depth<B, TC>::value;
-    constexpr int NDW = B * Tile<TC>::NQ;
+                                          float (&yacc)[Rows<MB, TC>::YB][4]) {
+    constexpr bool MMA = Rows<MB, TC>::MMA;
+    constexpr int DEPTH = MMA ? 2 : Depth<B, TC>::value;
+    constexpr int NDW = MMA ? 4 * B : B * Tile<TC>::NQ;
+    constexpr int NS = MMA ? 4 : 1;             // scales per lane and group
+    constexpr int NX = MMA ? 4 : MB;            // activation operands per lane and group
     uint32_t Q[DEPTH][NDW];
-    uint16_t S[DEPTH];
-    u4v X[DEPTH][MB];
+    uint16_t S[DEPTH][NS];
+    u4v X[DEPTH][NX];
     const EXQ_GLOBAL uint32_t* og = gptr<uint32_t>(ord);
     const uint32_t N16 = 16u * (uint32_t)L.N;
-    auto issue = [&](int step, uint32_t (&Qd)[NDW], uint16_t& Sd, u4v (&Xd)[MB]) {
+    auto issue = [&](int step, uint32_t (&Qd)[NDW], uint16_t (&Sd)[NS], u4v (&Xd)[NX]) {
         const bool valid = step < cnt;
         const uint32_t e = og[min(step, cnt - 1)];
         const uint32_t g = e & 0xFFFFu, P = e >> 16;
-        const uint32_t col = valid ? 16u * ((uint32_t)L.N * P + (uint32_t)c.n) : kBufOOB;
-        if constexpr (TC == 64) load_group_words<B>(c.rw, col, N16, Qd);
-        else load_quarter<B>(c.rw, col, N16, c.q, Qd);
-        if constexpr (QS) {
-            const uint32_t soff = valid ? g * ((uint32_t)L.N >> 1) + ((uint32_t)c.n >> 1) : kBufOOB;
-            Sd = (uint16_t)__builtin_amdgcn_raw_buffer_load_b8(c.rs, soff, 0, 0);
-        } else {
-            const uint32_t soff = valid ? 2u * (g * (uint32_t)L.N + (uint32_t)c.n) : kBufOOB;
-            Sd = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(c.rs, soff, 0, 0);
-        }
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb) Xd[rb] = load_act<TC>(L, c, (int)g, rb);
+        for (int cb = 0; cb < NS; ++cb) {
+            const uint32_t n = (uint32_t)(c.n + 16 * cb);
+            const uint32_t col = valid ? 16u * ((uint32_t)L.N * P + n) : kBufOOB;
+            if constexpr (MMA) load_quarter<B>(c.rw, col, N16, c.q, *reinterpret_cast<uint32_t(*)[B]>(Qd + cb * B));
+            else if constexpr (TC == 64) load_group_words<B>(c.rw, col, N16, Qd);
+            else load_quarter<B>(c.rw, col, N16, c.q, Qd);
+            if constexpr (QS) {
+                const uint32_t soff = valid ? g * ((uint32_t)L.N >> 1) + (n >> 1) : kBufOOB;
+                Sd[cb] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b8(c.rs, soff, 0, 0);
+            } else {
+                const uint32_t soff = valid ? 2u * (g * (uint32_t)L.N + n) : kBufOOB;
+                Sd[cb] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(c.rs, soff, 0, 0);
+            }
+        }
+        if constexpr (MMA) {
+            const int row = min(c.lane & 15, c.M - 1);   // rows past M repeat row M-1 (unused)
+            const EXQ_GLOBAL u4v* xr = gptr<u4v>(L.x + (size_t)row * L.K + (size_t)g * kGroup + 32 * c.q);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) Xd[kk] = xr[kk];
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) Xd[rb] = load_act<TC>(L, c, (int)g, rb);
+        }
     };
     static_for<0, DEPTH - 1>([&](auto KC) {
         constexpr int k = decltype(KC)::value;
@@ -231,7 +313,8 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
                 return;
             }
             issue(i + k + DEPTH - 1, Q[nk], S[nk], X[nk]);
-            group_compute<B, MB, TC, M1, QS>(c, Q[k], X[k], S[k], yacc);
+            if constexpr (MMA) group_compute_mma<B, QS>(c, Q[k], X[k], S[k], yacc);
+            else group_compute<B, MB, TC, M1, QS>(c, Q[k], X[k], S[k][0], yacc);
         });
     }
 }
@@ -244,23 +327,33 @@ template <int MB, int TC, bool M1, bool QS>
 __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int M, float* red) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr bool MMA = Rows<MB, TC>::MMA;
+    constexpr int YB = Rows<MB, TC>::YB;
     DecodeCtx c;
     c.M = M;
     c.lane = lane;
-    c.q = TC == 64 ? 0 : lane >> 4;
-    c.n = tile * TC + (TC == 64 ? lane : (lane & 15));
+    c.q = (TC == 64 && !MMA) ? 0 : lane >> 4;
+    c.n = tile * TC + ((TC == 64 && !MMA) ? lane : (lane & 15));
     c.rw = buffer_rsrc(L.qweight, L.qbytes);
+    c.ref = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) c.ref4[cb] = 0.0f;
     if constexpr (QS) {
         c.rs = buffer_rsrc(L.qscale, L.qsbytes);
-        c.ref = (float)__builtin_bit_cast(_Float16, gptr<uint16_t>(L.ref)[c.n]);
+        if constexpr (MMA) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                c.ref4[cb] = (float)__builtin_bit_cast(_Float16, gptr<uint16_t>(L.ref)[c.n + 16 * cb]);
+        } else {
+            c.ref = (float)__builtin_bit_cast(_Float16, gptr<uint16_t>(L.ref)[c.n]);
+        }
     } else {
         c.rs = buffer_rsrc(L.scales, L.sbytes);
-        c.ref = 0.0f;
     }
 
-    float yacc[MB][4];
+    float yacc[YB][4];
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb)
+    for (int rb = 0; rb < YB; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) yacc[rb][r] = 0.f;
     {
@@ -275,6 +368,17 @@ __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int 
         if ((k = cnt[5]) > 0) { run_width<8, MB, TC, M1, QS>(L, c, ord, k, yacc); }
     }
 
+    // 16-row layout: every (row, column) of the tile belongs to one lane.
+    if constexpr (MMA) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * c.q + i;
+                if (row < M) red[(wave * M + row) * TC + (lane & 15) + 16 * cb] = yacc[cb][i];
+            }
+        return;
+    }
     // TC = 16: quarters ((q0 + q1) + (q2 + q3)) in every lane of a column.
     // Then waves, in order, through LDS.
 #pragma unroll
@@ -317,7 +421,8 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // linear's groups, then the same share of the up linear's, into two sets of
 // partials; the workgroup then writes h = SiLU(g) * u for its TC columns.
 template <int MB, int TC, bool M1, bool QS>
-__global__ __launch_bounds__(kWaves * 64) void gated_decode_kernel(LinearDev G, LinearDev U, int M) {
+__global__ __launch_bounds__(kWaves * 64, (Rows<MB, TC>::WAVES_PER_EU)) void gated_decode_kernel(LinearDev G, LinearDev U,
+                                                                                        int M) {
     __shared__ float red[2][kWaves * 4 * MB * TC];
     decode_stream<MB, TC, M1, QS>(G, blockIdx.x, M, red[0]);
     decode_stream<MB, TC, M1, QS>(U, blockIdx.x, M, red[1]);
@@ -330,13 +435,13 @@ __global__ __launch_bounds__(kWaves * 64) void gated_decode_kernel(LinearDev G, 
 }
 
 template <int MB, int TC, bool M1, bool QS>
-__global__ __launch_bounds__(kWaves * 64) void decode_kernel(LinearDev L, int M) {
+__global__ __launch_bounds__(kWaves * 64, (Rows<MB, TC>::WAVES_PER_EU)) void decode_kernel(LinearDev L, int M) {
     __shared__ float red[kWaves * 4 * MB * TC];
     decode_wg<MB, TC, M1, QS>(L, blockIdx.x, M, red);
 }
 
 template <int MB, bool M1, bool QS>
-__global__ __launch_bounds__(kWaves * 64) void decode_plan_kernel(const LinearDev* __restrict__ list,
+__global__ __launch_bounds__(kWaves * 64, (Rows<MB, 64>::WAVES_PER_EU)) void decode_plan_kernel(const LinearDev* __restrict__ list,
                                                                    const uint32_t* __restrict__ wg_map, int M) {
     __shared__ float red[kWaves * 4 * MB * 64];
     const uint32_t e = gptr<uint32_t>(wg_map)[blockIdx.x];   // linear | tile << 16
@@ -522,7 +627,8 @@ namespace {
 // that still gives a workgroup per CU, or half that from 4 rows on (where the
 // wider tile's shared activation loads pay for the emptier machine: measured
 // 1.2x at 4 rows and 1.6x at 16 on 8192 columns); else 16.
-int tile_cols_for(int N, int m) { return (N / 64 >= 256 || (m >= 4 && N / 64 >= 128)) ? 64 : 16; }
+// 64 columns for wide layers, and always above 4 rows (the 16-row MFMA layout).
+int tile_cols_for(int N, int m) { return (m > 4 || N / 64 >= 256 || (m >= 4 && N / 64 >= 128)) ? 64 : 16; }
 
 template <int MB, int TC, bool M1>
 void launch_decode_t(LinearDev d, int M, hipStream_t stream) {

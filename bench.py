@@ -445,7 +445,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only (the library has no multi-GPU path); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

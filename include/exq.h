@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
     EXQ_OK = 0,
     EXQ_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad width, non-finite input */
-    EXQ_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (e.g. group size != 128) */
+    EXQ_ERR_UNSUPPORTED = 2, /* a valid request the library does not implement (e.g. group size != 128) */
     EXQ_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
     EXQ_ERR_OOM = 4          /* device or host allocation failed */
 } exq_status;

@@ -8,16 +8,17 @@ import numpy as np
 
 import oracle
 
-LOG = os.environ.get("EXQ_TEST_LOG", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                                                  "gpurun_out", "test_progress.log"))
+LOG = os.environ.get("EXQ_TEST_LOG")   # optional progress file, e.g. one that outlives a crashed run
 
 
 def note(msg: str) -> None:
-    """Name the case before a GPU step, on stderr and in a progress file."""
+    """Name the case before a GPU step, on stderr and, if EXQ_TEST_LOG is set, in that file."""
     sys.stderr.write("[exq-test] %s\n" % msg)
     sys.stderr.flush()
+    if not LOG:
+        return
     try:
-        os.makedirs(os.path.dirname(LOG), exist_ok=True)
+        os.makedirs(os.path.dirname(os.path.abspath(LOG)), exist_ok=True)
         with open(LOG, "a") as f:
             f.write(msg + "\n")
     except OSError:

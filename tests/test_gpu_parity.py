@@ -193,6 +193,30 @@ def test_plan_matches_oracle_and_is_repeatable(exq):
         l.close()
 
 
+def test_plan_with_shared_input(exq):
+    """q/k/v-style: several linears of one K read the same x in one plan launch."""
+    specs = [(640, 192, [2, 3, 8, 2, 5]), (640, 64, [6, 2, 2, 4, 3]), (640, 64, [3, 3, 2, 2, 2])]
+    layers, refs = [], []
+    for i, (K, N, widths) in enumerate(specs):
+        W = synth.weight(synth.seed_for("plan-shared", i), N, K)
+        layer, codes, s_ref, _ = make_layer(exq, W, widths)
+        layers.append(layer)
+        refs.append(oracle.dequant(codes, s_ref, widths))
+    for M in (1, 7, 16):
+        x_h = synth.activations(synth.seed_for("plan-shared-x", M), M, 640)
+        x = to_dev(x_h)
+        ys = [torch.empty((M, l.N), dtype=torch.float16, device="cuda") for l in layers]
+        note("plan with shared input M=%d" % M)
+        plan = exq.Plan(layers, [x] * len(layers), ys, M)
+        plan.run()
+        for y, w_ref, l in zip(ys, refs, layers):
+            y_ref, bnd = oracle.gemm(x_h, w_ref)
+            assert_within(y_to_np(y), y_ref, bnd, "shared-input plan M=%d N=%d" % (M, l.N))
+        plan.close()
+    for l in layers:
+        l.close()
+
+
 def test_runtime_errors_on_device(exq):
     W = synth.weight(synth.seed_for("err"), 64, 256)
     layer, *_ = make_layer(exq, W, [2, 4])

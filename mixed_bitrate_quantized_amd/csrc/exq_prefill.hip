@@ -399,6 +399,9 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
         T0 = T4;
     }
     mfma_ops(carry, acc);
+    // The last stages' copies (of clamped stages, never read) land before
+    // the tile ends, so none can reach the LDS of the next workgroup.
+    __builtin_amdgcn_s_waitcnt((0 & 15) | ((0 >> 4) << 14) | (7 << 4) | (15 << 8));   // vmcnt(0)
 
     // Epilogue: lane holds rows m = 32 jb + lane % 32 and, per a, four
     // consecutive columns n = 64 wave + 32 ib + 8 a + 4 (lane / 32) + [0, 4).

@@ -230,3 +230,22 @@ def test_runtime_errors_on_device(exq):
     with pytest.raises(exq.ExqError):
         exq.exq_gemm(x.data_ptr() + 2, 1, layer.handle, x.data_ptr() + 4096)
     layer.close()
+
+
+def test_seeded_random_shapes(exq):
+    """A seeded sweep of shapes, widths and row counts across the three kernel
+    paths (4x4x4 decode, 16-row MFMA decode, prefill), against the oracle."""
+    rng = np.random.default_rng(20261203)
+    for case in range(24):
+        G = int(rng.integers(1, 13))
+        K, N = 128 * G, 64 * int(rng.integers(1, 10))
+        widths = [int(b) for b in rng.choice([2, 3, 4, 5, 6, 8], size=G)]
+        M = int(rng.choice([1, 2, 3, 4, 5, 8, 11, 16, 17, 40, 64, 65, 129, 300]))
+        W = synth.weight(synth.seed_for("random-shapes", case), N, K)
+        layer, codes, s_ref, _ = make_layer(exq, W, widths)
+        x = synth.activations(synth.seed_for("random-shapes-x", case), M, K)
+        note("random shape %d: K=%d N=%d M=%d widths=%s" % (case, K, N, M, widths))
+        y = y_to_np(layer.gemm(to_dev(x)))
+        y_ref, bnd = oracle.gemm(x, oracle.dequant(codes, s_ref, widths))
+        assert_within(y, y_ref, bnd, "random shape %d (K=%d N=%d M=%d)" % (case, K, N, M))
+        layer.close()

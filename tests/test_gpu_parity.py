@@ -249,3 +249,37 @@ def test_seeded_random_shapes(exq):
         y_ref, bnd = oracle.gemm(x, oracle.dequant(codes, s_ref, widths))
         assert_within(y, y_ref, bnd, "random shape %d (K=%d N=%d M=%d)" % (case, K, N, M))
         layer.close()
+
+
+def test_seeded_random_plans(exq):
+    """Seeded plans of 1-5 linears of random shapes and widths, decode and
+    prefill row counts, against the oracle and repeatable bit for bit."""
+    rng = np.random.default_rng(31)
+    for case in range(8):
+        count = int(rng.integers(1, 6))
+        M = int(rng.choice([1, 3, 6, 16, 20, 256, 300]))
+        layers, refs, xs_h = [], [], []
+        for i in range(count):
+            G = int(rng.integers(1, 9))
+            K, N = 128 * G, 64 * int(rng.integers(1, 7))
+            widths = [int(b) for b in rng.choice([2, 3, 4, 5, 6, 8], size=G)]
+            W = synth.weight(synth.seed_for("random-plan", case, i), N, K)
+            layer, codes, s_ref, _ = make_layer(exq, W, widths)
+            layers.append(layer)
+            refs.append(oracle.dequant(codes, s_ref, widths))
+            xs_h.append(synth.activations(synth.seed_for("random-plan-x", case, i), M, K))
+        xs = [to_dev(x) for x in xs_h]
+        ys = [torch.empty((M, l.N), dtype=torch.float16, device="cuda") for l in layers]
+        note("random plan %d: %d linears, M=%d" % (case, count, M))
+        plan = exq.Plan(layers, xs, ys, M)
+        plan.run()
+        got = [y_to_np(y).copy() for y in ys]
+        for x, g, w_ref, l in zip(xs_h, got, refs, layers):
+            y_ref, bnd = oracle.gemm(x, w_ref)
+            assert_within(g, y_ref, bnd, "random plan %d M=%d N=%d" % (case, M, l.N))
+        plan.run()
+        for y, g in zip(ys, got):
+            np.testing.assert_array_equal(y_to_np(y), g)
+        plan.close()
+        for l in layers:
+            l.close()

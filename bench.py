@@ -33,6 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_plan_70b_m1_counters.json")
 PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_plan_70b_m2048_counters.json")
+# The prefill kernel and the plan builder that orders its tiles (the order sets its traffic).
+PREFILL_SOURCES = ("exq_prefill.hip", "exq_device.hip", "exq_device_common.h", "exq_internal.h")
 
 
 STREAM_READ_WGS = 8192   # workgroups of the streaming-read diagnostic (about 35 KB each per 286 MB)
@@ -392,7 +394,7 @@ def prefill_leg(exq, torch, steps, warmup):
     if os.path.exists(PREFILL_COUNTERS):
         with open(PREFILL_COUNTERS) as f:
             prof = json.load(f)
-        if prof.get("kernel_source_hash") == kernel_source_hash(("exq_prefill.hip", "exq_device_common.h", "exq_internal.h")):
+        if prof.get("kernel_source_hash") == kernel_source_hash(PREFILL_SOURCES):
             traffic = prof.get("hbm_bytes_per_launch")
     log("prefill step %.3f ms, %.1f TFLOP/s; launch %.3f ms (%.1f TFLOP/s); 7 calls %.3f ms" % (
         ms_step, tflops, kernel_ms, achieved, ms_calls))

@@ -1052,31 +1052,27 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
             for (int t = 0; t < list[i].tiles; ++t) wg_map.push_back((uint32_t)i | ((uint32_t)t << 16));
     } else {
         // Workgroup ids are dispatched to the 8 XCDs round-robin (id % 8).  Each
-        // linear's tiles are cut into 2 row groups x 4 column groups (1 x 8
-        // for a single row tile), and each block goes, whole, to the
-        // least-loaded XCD with its rows varying fastest: the tiles running
-        // together on an XCD share a column tile of W and the row tiles of x
-        // through its L2.  W is then fetched about twice and x four times
-        // instead of W eight times (one row tile per XCD): 21 % less HBM
-        // traffic on the 70B block at M = 2048, at the same speed.  Entry i is
-        // the next tile queued for XCD i % 8; short queues are padded with
-        // empty entries (kPlanEmpty: the workgroup exits at once).
+        // block of a linear's tiles (xcd_block: 2 row groups x 4 column
+        // groups) goes, whole, to the least-loaded XCD with its rows varying
+        // fastest, so the tiles running together on an XCD share a column tile
+        // of W and the row tiles of x through its L2.  W is then fetched about
+        // twice and x four times instead of W eight times (one row tile per
+        // XCD): 21 % less HBM traffic on the 70B block at M = 2048, at the same
+        // speed.  Entry i is the next tile queued for XCD i % 8; short queues
+        // are padded with empty entries (kPlanEmpty: the workgroup exits).
         std::vector<std::vector<uint32_t>> queue(kXcds);
         std::vector<long> load(kXcds, 0);
         for (int i : byw) {
             const int col_tiles = (layers[i]->N + 255) / 256, row_tiles = list[i].tiles / col_tiles;
-            const int RG = std::min(row_tiles, 2), CG = kXcds / RG;
-            for (int rg = 0; rg < RG; ++rg)
-                for (int cg = 0; cg < CG; ++cg) {
-                    const int r0 = row_tiles * rg / RG, r1 = row_tiles * (rg + 1) / RG;
-                    const int c0 = col_tiles * cg / CG, c1 = col_tiles * (cg + 1) / CG;
-                    if (r0 == r1 || c0 == c1) continue;
-                    const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-                    for (int ct = c0; ct < c1; ++ct)
-                        for (int r = r0; r < r1; ++r)
-                            queue[x].push_back((uint32_t)i | ((uint32_t)(r * col_tiles + ct) << 16));
-                    load[x] += (long)(r1 - r0) * (c1 - c0) * work[i];
-                }
+            for (int blk = 0; blk < kXcds; ++blk) {
+                const XcdBlock b = xcd_block(row_tiles, col_tiles, blk);
+                if (b.nr == 0 || b.nc == 0) continue;
+                const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+                for (int ct = b.c0; ct < b.c0 + b.nc; ++ct)
+                    for (int r = b.r0; r < b.r0 + b.nr; ++r)
+                        queue[x].push_back((uint32_t)i | ((uint32_t)(r * col_tiles + ct) << 16));
+                load[x] += (long)b.nr * b.nc * work[i];
+            }
         }
         size_t longest = 0;
         for (const auto& q : queue) longest = std::max(longest, q.size());

@@ -17,6 +17,20 @@ constexpr int kWaves = 8;       // waves per decode workgroup, each takes a shar
 constexpr int kMaxDecodeM = 16; // largest M served by the decode kernel
 constexpr int kTuneMaxM = 64;   // row counts a layer keeps a tuned kernel choice for
 
+// Prefill tiles of one linear by XCD: block b of 8 is rows [r0, r0 + nr) x
+// columns [c0, c0 + nc) of the (row tiles x column tiles) grid, from 2 row
+// groups x 4 column groups (1 x 8 for a single row tile).  Tiles of one
+// block run on one XCD, rows varying fastest, and share W and x in its L2.
+struct XcdBlock {
+    int r0, nr, c0, nc;
+};
+constexpr XcdBlock xcd_block(int row_tiles, int col_tiles, int b) {
+    const int rgs = row_tiles < 2 ? 1 : 2, cgs = 8 / rgs, rg = b / cgs, cg = b % cgs;
+    const int r0 = row_tiles * rg / rgs, r1 = row_tiles * (rg + 1) / rgs;
+    const int c0 = col_tiles * cg / cgs, c1 = col_tiles * (cg + 1) / cgs;
+    return XcdBlock{r0, r1 - r0, c0, c1 - c0};
+}
+
 // Kernel choices of exq_gemm (a layer's tuned entry for M, 0 = the default rule).
 enum Variant : uint8_t { kVarDefault = 0, kVarDecode16 = 1, kVarDecode64 = 2, kVarPrefill = 3, kNumVariants = 4 };
 

@@ -29,6 +29,7 @@
 //     tile are shared through that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 
 #include "exq_device_common.h"
@@ -439,11 +440,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, 
     __shared__ __attribute__((aligned(1024))) uint16_t sxb[kPXBytes / 2];
     __shared__ __attribute__((aligned(1024))) uint16_t sxc[kPXBytes / 2];
     __shared__ __attribute__((aligned(1024))) uint16_t sxd[kPXBytes / 2];
-    // XCD-aware tile order: ids i, i+8, i+16, ... (one XCD) take consecutive tiles.
-    const int T = row_tiles * col_tiles;
-    const int i = blockIdx.x, xcd = i & 7, per = T >> 3, rem = T & 7;
-    const int t = xcd * per + min(xcd, rem) + (i >> 3);
-    prefill_tile<GATED>(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sxa, sxb, sxc, sxd);
+    // XCD-aware tile order: ids x, x+8, x+16, ... (XCD x) take block x of
+    // xcd_block, rows varying fastest; ids past a smaller block exit.
+    const int j = (int)(blockIdx.x >> 3);
+    const XcdBlock b = xcd_block(row_tiles, col_tiles, (int)(blockIdx.x & 7));
+    if (j >= b.nr * b.nc) return;
+    prefill_tile<GATED>(L, M, (b.r0 + j % b.nr) * kPT, (b.c0 + j / b.nr) * kPT, sxa, sxb, sxc, sxd);
 }
 
 // Several linears in one launch: workgroup i takes entry i of wg_map
@@ -485,8 +487,13 @@ exq_status prefill_launch(const exq_layer* L, const void* x, int M, void* y, hip
     const long row_tiles = (M + kPT - 1) / kPT, col_tiles = (L->N + kPT - 1) / kPT;
     if (row_tiles * col_tiles > INT_MAX) return fail(EXQ_ERR_UNSUPPORTED, "M=%d gives too many tiles", M);
     LinearDev d = linear_dev(L, x, y);
-    hipLaunchKernelGGL(prefill_kernel<GATED>, dim3((unsigned)(row_tiles * col_tiles)), dim3(kPThreads), 0, stream, d,
-                       M, (int)row_tiles, (int)col_tiles);
+    long per_xcd = 0;   // the largest block: 8 of them cover every tile
+    for (int blk = 0; blk < 8; ++blk) {
+        const XcdBlock b = xcd_block((int)row_tiles, (int)col_tiles, blk);
+        per_xcd = std::max(per_xcd, (long)b.nr * b.nc);
+    }
+    hipLaunchKernelGGL(prefill_kernel<GATED>, dim3((unsigned)(8 * per_xcd)), dim3(kPThreads), 0, stream, d, M,
+                       (int)row_tiles, (int)col_tiles);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? EXQ_OK : fail(EXQ_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
 }

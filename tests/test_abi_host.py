@@ -138,3 +138,40 @@ def test_trimmed_mean_definition():
     assert exq.exq_trimmed_mean([4.0]) == 4.0
     assert exq.exq_trimmed_mean([2.0, 6.0]) == 4.0
     assert exq.exq_trimmed_mean([]) == -1.0
+
+
+def test_xcd_blocks_partition_every_tile_grid(tmp_path):
+    """The prefill launches' XCD blocks (xcd_block in the internal header):
+    for every grid up to 40 x 120 tiles the 8 blocks cover each tile once."""
+    import shutil
+    import subprocess
+    cxx = shutil.which("g++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    header = os.path.join(os.path.dirname(exq.__file__), "csrc", "exq_internal.h")
+    src = tmp_path / "xcd_blocks.cpp"
+    src.write_text('''#include "%s"
+#include <cstdio>
+#include <vector>
+int main() {
+    for (int R = 1; R <= 40; ++R)
+        for (int C = 1; C <= 120; ++C) {
+            std::vector<int> seen(R * C, 0);
+            for (int b = 0; b < 8; ++b) {
+                const exq::XcdBlock x = exq::xcd_block(R, C, b);
+                if (x.nr < 0 || x.nc < 0) return 1;
+                for (int r = x.r0; r < x.r0 + x.nr; ++r)
+                    for (int c = x.c0; c < x.c0 + x.nc; ++c) {
+                        if (r < 0 || r >= R || c < 0 || c >= C) return 2;
+                        ++seen[r * C + c];
+                    }
+            }
+            for (int v : seen)
+                if (v != 1) return 3;
+        }
+    return 0;
+}
+''' % header)
+    exe = tmp_path / "xcd_blocks"
+    subprocess.run([cxx, "-std=c++17", "-O1", "-o", str(exe), str(src)], check=True)
+    assert subprocess.run([str(exe)]).returncode == 0

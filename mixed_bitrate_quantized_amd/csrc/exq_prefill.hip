@@ -95,8 +95,11 @@ struct QRegs {
 // Loads quarter 2h + j of the lane's two columns through fixed slots; a slot
 // the width does not use reads an out-of-range offset (zeros, no traffic).
 // Column-local dword m of group g sits at byte 16 (N P_g + (m / 4) N + n) + 4 (m % 4).
+// SAME_GROUP: the stage is the second half of the group `prev` was loaded
+// for (stages run in pairs from an even one), so its scale is prev's.
+template <bool SAME_GROUP>
 __device__ __forceinline__ void issue_w(const LinearDev& L, const PrefillCtx& c, const StageSrc& src,
-                                        QRegs (&W)[2]) {
+                                        QRegs (&W)[2], const QRegs (&prev)[2]) {
     const int b = src.b;
     const uint32_t p0 = b <= 3 ? 2u : (b == 8 ? 8u : 4u), p1 = (uint32_t)b - p0;
     const uint32_t N16 = 16u * (uint32_t)L.N, qq = 2u * src.h + c.q;
@@ -119,8 +122,10 @@ __device__ __forceinline__ void issue_w(const LinearDev& L, const PrefillCtx& c,
         W[i].q[7] = bq[3];
         W[i].h[0] = hh[0];
         W[i].h[1] = hh[1];
-        W[i].s = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
-            c.rs, src.so + 2u * c.col[i], 0, 0);
+        if constexpr (SAME_GROUP)
+            W[i].s = prev[i].s;   // the second half of a group: the first half's scale
+        else
+            W[i].s = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(c.rs, src.so + 2u * c.col[i], 0, 0);
     }
 }
 
@@ -269,12 +274,13 @@ __device__ __forceinline__ void region_schedule() {
 // stage st+1) are loaded at the very end and first used after the closing
 // barrier, whose wait covers them: scalar loads return out of order, so
 // while one is outstanding every wait for an operand read would drain all.
+template <bool NEXT_SAME_GROUP>
 __device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx& c, int st, int S,
                                            const uint16_t* rd_x, uint16_t* wr_x, const QRegs (&Wc)[2],
                                            QRegs (&Wn)[2], const StageSrc& src1, const StageSrc& src2,
                                            const DqRow& T, StageSrc& src3, DqRow& T_n, Ops& carry, Ops& other,
                                            f16v (&acc)[2][8]) {
-    issue_w(L, c, src1, Wn);
+    issue_w<NEXT_SAME_GROUP>(L, c, src1, Wn, Wc);
     static_for<0, 4>([&](auto KC) {
         constexpr int KK = decltype(KC)::value;
         Ops& rd = (KK & 1) ? carry : other;     // K-step KK lands here
@@ -293,10 +299,11 @@ __device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx&
     T_n = kDq[src1.b];
 }
 
-// Closes a stage.  A stage issues 16 vector memory operations (8 packed-word
-// loads, 8 copies), so waiting until at most 8 are outstanding completes
-// every one issued before it -- in particular the copies of the x tile the
-// next stage reads; then the barrier makes the copies of all waves visible.
+// Closes a stage.  A stage issues at least 14 vector memory operations (6 or
+// 8 packed-word and scale loads, 8 copies), so waiting until at most 8 are
+// outstanding completes every one issued before it -- in particular the
+// copies of the x tile the next stage reads; then the barrier makes the
+// copies of all waves visible.
 // The copies write LDS behind the compiler's back as far as __syncthreads is
 // concerned (its fence would wait for all of them), hence the explicit wait
 // and a bare barrier; sched_barrier keeps the next stage's reads below it.
@@ -374,7 +381,7 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
                 *reinterpret_cast<u4v*>(reinterpret_cast<char*>(sxb) + 16 * (k * kPThreads + c.tid)) = z;
             }
         }
-        issue_w(L, c, s0, W0);
+        issue_w<false>(L, c, s0, W0, W0);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
     // Zero operands: the first stage's region 0 adds exact zeros.
@@ -387,13 +394,13 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
     for (int st = st0; st < S; st += 4) {
         StageSrc s3, s4, s5, s6;
         DqRow T1, T2, T3, T4;
-        stage_body(L, c, st, S, sxa, sxc, W0, W1, s1, s2, T0, s3, T1, carry, other, acc);
+        stage_body<true>(L, c, st, S, sxa, sxc, W0, W1, s1, s2, T0, s3, T1, carry, other, acc);
         stage_end();
-        stage_body(L, c, st + 1, S, sxb, sxd, W1, W0, s2, s3, T1, s4, T2, carry, other, acc);
+        stage_body<false>(L, c, st + 1, S, sxb, sxd, W1, W0, s2, s3, T1, s4, T2, carry, other, acc);
         stage_end();
-        stage_body(L, c, st + 2, S, sxc, sxa, W0, W1, s3, s4, T2, s5, T3, carry, other, acc);
+        stage_body<true>(L, c, st + 2, S, sxc, sxa, W0, W1, s3, s4, T2, s5, T3, carry, other, acc);
         stage_end();
-        stage_body(L, c, st + 3, S, sxd, sxb, W1, W0, s4, s5, T3, s6, T4, carry, other, acc);
+        stage_body<false>(L, c, st + 3, S, sxd, sxb, W1, W0, s4, s5, T3, s6, T4, carry, other, acc);
         stage_end();
         s1 = s5;
         s2 = s6;

@@ -43,6 +43,11 @@
  *   - arguments are validated before anything is launched; a failed call
  *     launches nothing and leaves outputs untouched.
  *   - results are deterministic: the same inputs give the same bits.
+ *   - exq_gemm, exq_gemm_gated, exq_dequant and exq_plan_run launch kernels
+ *     only (no allocation, memset or wait), so they may be captured in a HIP
+ *     graph, whose replays then read and write the buffers bound at capture.
+ *     The one exception is the first call that expands a layer's quantized
+ *     scales (exq_layer_create_qs below): make it before capturing.
  */
 #ifndef EXQ_H
 #define EXQ_H

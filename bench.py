@@ -259,7 +259,7 @@ def autotune_leg(exq, torch, layers, stream, Ms=(1, 4, 16, 32)):
             y = torch.empty((M, N), dtype=torch.float16, device="cuda")
             choice, times = exq.exq_autotune(x.data_ptr(), M, lay.handle, y.data_ptr(), stream, 20, 200)
             m = min(M, 16)   # exq_gemm's default: decode slices of 16 rows, this tile rule
-            default = 2 if (N // 64 >= 256 or (m >= 4 and N // 64 >= 128)) else 1
+            default = 2 if (m > 4 or N // 64 >= 256 or (m >= 4 and N // 64 >= 128)) else 1
             rows.append({"linear": name, "choice": names[choice - 1], "us": round(times[choice - 1], 2),
                          "default_us": round(times[default - 1], 2),
                          "candidates_us": [round(t, 2) for t in times]})

@@ -230,9 +230,10 @@ exq_status exq_gemm_gated(const void* x, int M, exq_layer_t gate, exq_layer_t up
  * variants the first time a shape is seen -- 20 warmup and 200 timed runs
  * each -- keeps the one with the lowest interquartile-style mean (the mean of
  * the samples between the 5/16 and 11/16 quantiles) and caches the choice.
- *   EXQ_VARIANT_DEFAULT   decode in 16-row slices, 64-column tiles when
- *                         N/64 >= 256, or N/64 >= 128 and a slice has >= 4
- *                         rows, else 16 (M <= 64 always takes this rule)
+ *   EXQ_VARIANT_DEFAULT   decode in 16-row slices, 64-column tiles when a
+ *                         slice has more than 4 rows, when N/64 >= 256, or
+ *                         when N/64 >= 128 and a slice has 4 rows; else 16
+ *                         (M <= 64 always takes this rule)
  *   EXQ_VARIANT_DECODE16  decode, 16-column tiles (16-row slices of x if M > 16)
  *   EXQ_VARIANT_DECODE64  decode, 64-column tiles (16-row slices of x if M > 16)
  *   EXQ_VARIANT_PREFILL   prefill kernel (M > 16 only)

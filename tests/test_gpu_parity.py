@@ -283,3 +283,32 @@ def test_seeded_random_plans(exq):
         plan.close()
         for l in layers:
             l.close()
+
+
+def test_plan_rejects_bad_arguments(exq):
+    """exq_plan_create validates before it allocates: an empty list, M < 1, a
+    misaligned buffer, an output overlapping an input or another output, and a
+    decode plan mixing fp16 and quantized scale storage are INVALID_ARG; the
+    corrected arguments make plans."""
+    W = synth.weight(synth.seed_for("plan-err"), 128, 256)
+    a, *_ = make_layer(exq, W, [3, 5])
+    b = exq.Layer.from_weight(W, [3, 5], quantized_scales=True)
+    buf = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    x0 = buf.data_ptr()
+    y0, y1 = x0 + 32768, x0 + 49152
+
+    def expect(handles, xs, ys, M):
+        with pytest.raises(exq.ExqError) as ei:
+            exq.exq_plan_create(handles, xs, ys, M)
+        assert ei.value.status == exq.EXQ_ERR_INVALID_ARG
+
+    expect([], [], [], 1)
+    expect([a.handle], [x0], [y0], 0)
+    expect([a.handle], [x0 + 2], [y0], 1)                        # misaligned x
+    expect([a.handle], [x0], [x0 + 256], 2)                      # y overlaps x
+    expect([a.handle, a.handle], [x0, x0], [y0, y0 + 128], 2)    # outputs overlap
+    expect([a.handle, b.handle], [x0, x0], [y0, y1], 1)          # decode plan, two scale storages
+    for handles, M in (([a.handle, a.handle], 2), ([a.handle, b.handle], 20), ([b.handle, b.handle], 1)):
+        exq.exq_plan_destroy(exq.exq_plan_create(handles, [x0, x0], [y0, y1], M))
+    a.close()
+    b.close()

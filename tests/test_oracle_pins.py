@@ -247,3 +247,38 @@ def test_quantizer_degenerate_groups():
     assert scales[1, 2] == 0 and np.all(codes[2, 128:] == 8)
     wh = oracle.dequant(codes, scales, widths)
     assert np.all(wh.view(np.float16)[np.arange(256) != 5] == 0)
+
+
+@pytest.mark.parametrize("b", WIDTHS)
+def test_quantizer_ties_round_to_even(b):
+    """Weights that put w/s exactly on a .5 tie, positive and negative, at every
+    width: the codes must follow ties-to-even (the quantizer reading R3), which
+    the distance inequality above cannot tell from ties-away-from-zero.  The
+    expected codes come from numpy's own rint (round-half-even) on fp32, a
+    route that shares nothing with the oracle's C code; the library packer is
+    held to the same codes."""
+    import mixed_bitrate_quantized_amd as exq
+    z, qmax = 1 << (b - 1), (1 << (b - 1)) - 1
+    s = np.float32(0.125)                               # a power of two: max|w| / qmax is exact
+    ties = (np.arange(-qmax, qmax, dtype=np.float32) + np.float32(0.5)) * s   # w / s = -qmax + .5 .. qmax - .5
+    N, K = 16, 256
+    W = np.empty((N, K), dtype=np.float32)
+    for n in range(N):
+        for g in range(K // 128):
+            blk = np.resize(np.roll(ties, 7 * n + 3 * g), 127)
+            top = qmax * s if (n + g) % 2 == 0 else -qmax * s   # the group maximum, either sign
+            W[n, 128 * g:128 * g + 128] = np.concatenate([[top], blk]).astype(np.float32)
+    widths = [b] * (K // 128)
+    codes, scales = oracle.quantize(W, widths)
+    assert np.all(scales.view(np.float16) == np.float16(s))
+    s16 = np.repeat(scales.view(np.float16).astype(np.float32).T, 128, axis=1)
+    r = np.float32(W) / s16
+    assert np.all(np.abs(r[:, 1::128] - np.floor(r[:, 1::128])) == 0.5)   # genuinely ties
+    want = (np.clip(np.rint(r), -qmax, qmax) + z).astype(np.uint8)
+    np.testing.assert_array_equal(codes, want)
+    # ties-away-from-zero would differ on every other tie
+    away = (np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), -qmax, qmax) + z).astype(np.uint8)
+    assert np.count_nonzero(away != want) >= N * (K // 128) * 127 // 3
+    q_lib, s_lib = exq.exq_pack(W, widths)
+    np.testing.assert_array_equal(s_lib, scales)
+    np.testing.assert_array_equal(oracle.unpack(q_lib, K, N, widths), want)

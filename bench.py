@@ -8,10 +8,17 @@ exq plan launch.  Inputs are seeded synthetic tensors of the model's shapes
 
 Prints one JSON line: whole-step HBM throughput (algorithmic bytes / step
 time), ms/step, the decode kernel's roofline and the CPU oracle timed on a
-bounded sample of the same workload.  A second leg ("prefill") times the
-prefill path on the same seven 70B shapes at M = 2048 tokens (mixed 4.0 bpw
-from {3,4,5,6}) against the fp16 matrix-core peak, and a third
-("batched_decode_m16") streams the same stack at M = 16 rows.
+bounded sample of the same workload.  Further legs:
+  * step_back_to_back: the same step as 560 exq_gemm calls back to back
+    (ungraphed and HIP-graph replayed), and as the launches a decoder
+    block's data flow allows (q/k/v plan, o, fused gate/up, down);
+  * prefill: the same seven 70B shapes at M = 2048 tokens (mixed 4.0 bpw
+    from {3,4,5,6}) against the fp16 matrix-core peak, with the oracle timed
+    on 64 seeded token rows;
+  * batched_decode_m16: the same stack at M = 16 rows;
+  * single_layer: configurations 1 (4096 x 4096, 4-bit, M = 1) and 2
+    (8192 x 8192, 2.55 bpw, M = 1/4/8/16), rotating over >= 1 GiB of copies;
+  * stream_read, gated_gate_up, quantized_scales, autotune, allocator.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 5|3] [--m 1] [--no-prefill] [--no-batched]
 """
@@ -85,6 +92,40 @@ def build_stack(exq, torch, specs, M, keep_first=0):
         if (i + 1) % 70 == 0 or i + 1 == len(specs):
             log("packed %d/%d linears (%.1f GB algorithmic) in %.0fs" % (i + 1, len(specs), total / 1e9, time.time() - t0))
     return layers, xs, ys, total, kept
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def event_timed(torch, stream, fn, reps, warmup=1):
+    """Mean ms of `fn` over `reps` back-to-back runs between two events on `stream`."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def graphed(torch, fn):
+    """`fn`'s launches captured once as a HIP graph (returns the graph)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return g
 
 
 def omp_threads() -> int:
@@ -354,14 +395,36 @@ def gated_leg(exq, torch, layers, xs, M, nblk, steps, stream):
             "bytes_per_step": nbytes}
 
 
-def prefill_leg(exq, torch, steps, warmup):
+def prefill_oracle_subset(kept, xs, ys, rows_n, seed):
+    """The oracle on `rows_n` seeded token rows of every linear, every output
+    column (its own packed layer; unpack + dequant + fp64 matmul timed), and
+    the worst error / tolerance of the GPU's rows."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    secs, flops, worst = 0.0, 0, 0.0
+    for (spec, W, widths), x, y in zip(kept, xs, ys):
+        _, s_ref, q_ref = oracle.reference_layer(W, widths)
+        rows = np.sort(rng.choice(x.shape[0], size=rows_n, replace=False))
+        xr = x[rows].cpu().numpy()
+        cols = np.arange(spec.N, dtype=np.int64)
+        t0 = time.perf_counter()
+        y_ref, bnd = oracle.gemm_packed_cols(xr, q_ref, s_ref, widths, spec.K, spec.N, cols)
+        secs += time.perf_counter() - t0
+        flops += 2 * rows_n * spec.K * spec.N
+        _, w = oracle.within_tolerance(y[rows].cpu().numpy().astype(np.float64), y_ref, bnd)
+        worst = max(worst, w)
+    return secs, flops, worst
+
+
+def prefill_leg(exq, torch, steps, warmup, oracle_rows=64):
     """The seven 70B-shaped linears at M = 2048 (mixed 4.0 bpw) as one prefill
     plan launch per step; step time, the launch's own duration, and the same
-    step as seven separate exq_gemm calls for reference."""
+    step as seven separate exq_gemm calls for reference.  The oracle is timed
+    on a seeded subset of token rows (every column of every linear)."""
     from synth import workloads
     M = workloads.M_VALUES[4][0]
     specs = workloads.linears(4)
-    layers, xs, ys, _, _ = build_stack(exq, torch, specs, M)
+    layers, xs, ys, _, kept = build_stack(exq, torch, specs, M, keep_first=len(specs) if oracle_rows else 0)
     flops = sum(2 * M * sp.K * sp.N for sp in specs)
     stream = torch.cuda.current_stream()
     plan = exq.Plan(layers, xs, ys, M)
@@ -385,6 +448,17 @@ def prefill_leg(exq, torch, steps, warmup):
         for l, x, y in zip(layers, xs, ys):
             exq.exq_gemm(x.data_ptr(), M, l.handle, y.data_ptr(), stream)
     ms_calls = timed(calls, max(3, steps // 2))
+    cpu = None
+    if oracle_rows:
+        plan.run(stream)
+        torch.cuda.synchronize()
+        log("timing the oracle on %d rows of each prefill linear" % oracle_rows)
+        secs, cflops, worst = prefill_oracle_subset(kept, xs, ys, oracle_rows, 4242)
+        cpu = {"value": round(cflops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": omp_threads(), "kind": "oracle",
+               "cpu_model": cpu_model(),
+               "sample": "%d seeded token rows of each of the 7 linears (of %d), every output column: bit-by-bit "
+                         "unpack + dequant + fp64 matmul from the oracle's own packed layer; %.1f s for %.3g flop; "
+                         "worst GPU error / tolerance on those rows %.3f" % (oracle_rows, M, secs, cflops, worst)}
     plan.close()
     for l in layers:
         l.close()
@@ -408,6 +482,7 @@ def prefill_leg(exq, torch, steps, warmup):
         "steps": steps,
         "warmup": warmup,
         "flops_per_step": flops,
+        "cpu_baseline": cpu,
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
@@ -420,6 +495,122 @@ def prefill_leg(exq, torch, steps, warmup):
             "avg_launch_ms": round(kernel_ms, 4),
         },
     }
+
+
+def back_to_back_leg(exq, torch, specs, layers, xs, ys, nblk, M, steps, stream, step_bytes):
+    """The step as a sequence of launches, every linear its own call:
+      * per_linear: the 560 (or 7) linears as exq_gemm calls back to back on
+        one stream, ungraphed and captured once as a HIP graph;
+      * dependent: the launches a decoder block's data flow allows -- q, k
+        and v as one plan on one shared x, then o, then gate and up fused
+        with their SiLU product (exq_gemm_gated), then down reading that
+        product -- ungraphed and graphed.  o's input (the attention output)
+        and gate/up's input (the next normalised hidden state) come from
+        outside this library and are fixed synthetic buffers.
+    Bytes per step are the headline's (the 560 linears' algorithmic bytes)."""
+    from synth import BLOCK_SHAPES
+    names = [b[0] for b in BLOCK_SHAPES]
+    per = len(names)
+    iq, ik, iv, io, ig, iu, idn = (names.index(n) for n in ("q", "k", "v", "o", "gate", "up", "down"))
+
+    def calls(st):
+        for l, x, y in zip(layers, xs, ys):
+            exq.exq_gemm(x.data_ptr(), M, l.handle, y.data_ptr(), st)
+
+    ms_calls = event_timed(torch, stream, lambda: calls(stream), steps)
+    g = graphed(torch, calls)
+    ms_calls_g = event_timed(torch, stream, g.replay, steps)
+    del g
+
+    blocks = []
+    for b in range(nblk):
+        L = layers[b * per:(b + 1) * per]
+        X = xs[b * per:(b + 1) * per]
+        Y = ys[b * per:(b + 1) * per]
+        h = torch.empty((M, L[ig].N), dtype=torch.float16, device="cuda")
+        qkv = exq.Plan([L[iq], L[ik], L[iv]], [X[iq], X[iq], X[iq]], [Y[iq], Y[ik], Y[iv]], M)
+        blocks.append((qkv, L, X, Y, h))
+
+    def dependent(st):
+        for qkv, L, X, Y, h in blocks:
+            qkv.run(st)
+            exq.exq_gemm(X[io].data_ptr(), M, L[io].handle, Y[io].data_ptr(), st)
+            exq.exq_gemm_gated(X[ig].data_ptr(), M, L[ig].handle, L[iu].handle, h.data_ptr(), st)
+            exq.exq_gemm(h.data_ptr(), M, L[idn].handle, Y[idn].data_ptr(), st)
+
+    ms_dep = event_timed(torch, stream, lambda: dependent(stream), steps)
+    g = graphed(torch, dependent)
+    ms_dep_g = event_timed(torch, stream, g.replay, steps)
+    del g
+    for qkv, *_ in blocks:
+        qkv.close()
+    del blocks
+    gbs = lambda ms: round(step_bytes / (ms * 1e-3) / 1e9, 1)
+    log("back to back: %d exq_gemm calls %.3f ms (graphed %.3f); dependent schedule %.3f ms (graphed %.3f)" % (
+        len(layers), ms_calls, ms_calls_g, ms_dep, ms_dep_g))
+    return {
+        "per_linear": {"launches_per_step": len(layers), "ms_per_step": round(ms_calls, 4), "GB/s": gbs(ms_calls),
+                       "ms_per_step_graphed": round(ms_calls_g, 4), "GB/s_graphed": gbs(ms_calls_g),
+                       "us_per_block": round(ms_calls * 1e3 / nblk, 2),
+                       "us_per_block_graphed": round(ms_calls_g * 1e3 / nblk, 2)},
+        "dependent": {"launches_per_step": 4 * nblk, "ms_per_step": round(ms_dep, 4), "GB/s": gbs(ms_dep),
+                      "ms_per_step_graphed": round(ms_dep_g, 4), "GB/s_graphed": gbs(ms_dep_g),
+                      "us_per_block": round(ms_dep * 1e3 / nblk, 2),
+                      "us_per_block_graphed": round(ms_dep_g * 1e3 / nblk, 2),
+                      "schedule": "per block: plan(q,k,v on one x) -> exq_gemm(o) -> exq_gemm_gated(gate,up) -> "
+                                  "exq_gemm(down on the gated output)"},
+        "steps": steps,
+    }
+
+
+def single_layer_leg(exq, torch, config, stream, reps=200, warmup=20, min_bytes=1 << 30):
+    """Configuration 1 or 2: one layer, exq_gemm at each M the configuration
+    names, rotating over distinct device copies of the packed layer totalling
+    at least 1 GiB (four times the 256 MB Infinity Cache), so every call reads
+    its weights from HBM.  `warmup` untimed and `reps` timed calls back to
+    back: the mean from two events around them, and the median and trimmed
+    mean (5/16-11/16 quantiles) of per-call event pairs in a second pass
+    (each pair adds its own few microseconds)."""
+    from synth import workloads
+    spec = workloads.linears(config)[0]
+    W = workloads.make_weight(spec)
+    widths = workloads.make_widths(spec, W)
+    q, sc = exq.exq_pack(W, widths)
+    per_copy = workloads.algorithmic_bytes(spec.K, spec.N, widths, 1)
+    copies = -(-min_bytes // per_copy)
+    layers = [exq.Layer(spec.K, spec.N, widths, q, sc) for _ in range(copies)]
+    out = {"workload": "%d -> %d, %s, %d rotating copies (%.2f GB)" % (
+        spec.K, spec.N, "uniform 4-bit" if spec.kind == "u4" else "mixed 2.55 bpw", copies,
+        copies * per_copy / 1e9), "rows": []}
+    for M in workloads.M_VALUES[config]:
+        x = torch.from_numpy(workloads.make_x(spec, M)).cuda()
+        y = torch.empty((M, spec.N), dtype=torch.float16, device="cuda")
+        it = [0]
+
+        def call():
+            l = layers[it[0] % copies]
+            it[0] += 1
+            exq.exq_gemm(x.data_ptr(), M, l.handle, y.data_ptr(), stream)
+
+        ms = event_timed(torch, stream, call, reps, warmup)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        samples = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+        nbytes = workloads.algorithmic_bytes(spec.K, spec.N, widths, M)
+        out["rows"].append({"M": M, "us_per_call": round(ms * 1e3, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                            "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                            "bytes_per_call": nbytes,
+                            "median_us_event_pairs": round(float(np.median(samples)), 3),
+                            "trimmed_mean_us_event_pairs": round(trimmed_mean(samples), 3)})
+    for l in layers:
+        l.close()
+    log("config %d: %s" % (config, ", ".join("M=%d %.2f us %.0f GB/s" % (r["M"], r["us_per_call"], r["GB/s"])
+                                             for r in out["rows"])))
+    return out
 
 
 def main():
@@ -435,8 +626,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum timed oracle work (the sample is repeated)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M = 2048 prefill leg")
     ap.add_argument("--no-batched", action="store_true", help="skip the M = 16 pass over the stack")
-    ap.add_argument("--prefill-steps", type=int, default=10)
-    ap.add_argument("--variants", action="store_true", help="also time per-linear calls, ungraphed and graphed")
+    ap.add_argument("--prefill-steps", type=int, default=50)
+    ap.add_argument("--prefill-warmup", type=int, default=10)
+    ap.add_argument("--prefill-oracle-rows", type=int, default=64, help="token rows the oracle is timed on (0: none)")
+    ap.add_argument("--no-back-to-back", action="store_true", help="skip the per-linear and dependent schedules")
+    ap.add_argument("--no-single", action="store_true", help="skip the single-layer rows (configurations 1 and 2)")
     ap.add_argument("--no-stream-read", action="store_true", help="skip the plain streaming-read ceiling")
     ap.add_argument("--no-gated", action="store_true", help="skip the fused gate/up (SiLU) leg")
     ap.add_argument("--no-allocator", action="store_true", help="skip the host bit-allocation leg")
@@ -588,37 +782,9 @@ def main():
         if prof.get("kernel_source_hash") == kernel_source_hash() and prof.get("config") == args.config and prof.get("m") == M:
             traffic = prof.get("hbm_bytes_per_launch")
 
-    extra = {}
-    if args.variants:
-        def timed(fn, reps):
-            fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / reps
-
-        reps = max(3, args.steps // 5)
-        whole = exq.Plan(layers, xs, ys, M)
-        extra["ms_per_step_one_launch"] = timed(lambda: whole.run(stream), reps)
-        whole.close()
-
-        def calls():
-            s = torch.cuda.current_stream()
-            for l, x, y in zip(layers, xs, ys):
-                exq.exq_gemm(x.data_ptr(), M, l.handle, y.data_ptr(), s)
-        extra["ms_per_step_separate_calls"] = timed(calls, reps)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            calls()
-        torch.cuda.synchronize()
-        extra["ms_per_step_separate_calls_graphed"] = timed(g.replay, reps)
-        del g
-        step()
-        torch.cuda.synchronize()
+    b2b = None
+    if not args.no_back_to_back:
+        b2b = back_to_back_leg(exq, torch, specs, layers, xs, ys, nblk, M, args.steps, stream, step_bytes)
 
     cpu = None
     if kept:
@@ -630,6 +796,7 @@ def main():
             "unit": "GB/s",
             "cores": omp_threads(),
             "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%d linears (block%s 0..%d of the same stack) at M=%d, every output column, %d passes: "
                       "bit-by-bit unpack + dequant + fp64 matmul from the oracle's own packed layer; %.1f s for "
                       "%.2f GB; worst GPU error / tolerance on the sample %.3f" % (
@@ -658,7 +825,13 @@ def main():
             l.close()
         del layers, xs, ys, plans
         torch.cuda.empty_cache()
-        prefill = prefill_leg(exq, torch, args.prefill_steps, 2)
+        prefill = prefill_leg(exq, torch, args.prefill_steps, args.prefill_warmup, args.prefill_oracle_rows)
+
+    single = None
+    if not args.no_single:
+        torch.cuda.empty_cache()
+        single = {"config1": single_layer_leg(exq, torch, 1, torch.cuda.current_stream()),
+                  "config2": single_layer_leg(exq, torch, 2, torch.cuda.current_stream())}
 
     out = {
         "metric": "quant GEMV eff. HBM GB/s (% peak) + ms/step, 70B-shaped 2.55bpw M=" + str(M),
@@ -679,6 +852,8 @@ def main():
             "linears": len(specs),
             "bytes_per_step": step_bytes,
             "launches_per_step": nblk,
+            "step": "one decode plan launch per block: the block's 7 linears, each on its own synthetic input, in "
+                    "one kernel (back-to-back and data-flow schedules in step_back_to_back)",
             "parallelism": "1 GPU",
         },
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -695,6 +870,8 @@ def main():
         },
         "ms_per_step_graphed": round(ms_step_graphed, 4),
         "step_stats": step_stats,
+        "step_back_to_back": b2b,
+        "single_layer": single,
         "stream_read": read,
         "gated_gate_up": gated,
         "batched_decode_m16": batched,
@@ -704,7 +881,6 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
     }
-    out.update(extra)
     print(json.dumps(out))
 
 

@@ -40,8 +40,8 @@
  *   - streams are hipStream_t values passed as void* (NULL = null stream).
  *     Launching calls are asynchronous and never synchronize; faults inside a
  *     kernel surface at the caller's next synchronization.
- *   - arguments are validated before anything is launched; a failed call
- *     launches nothing and leaves outputs untouched.
+ *   - arguments are validated before anything is launched; a call that
+ *     fails validation launches nothing and leaves outputs untouched.
  *   - results are deterministic: the same inputs give the same bits.
  *   - exq_gemm, exq_gemm_gated, exq_dequant and exq_plan_run launch kernels
  *     only (no allocation, memset or wait), so they may be captured in a HIP
@@ -160,7 +160,10 @@ exq_status exq_allocate_widths(const double* err, const int32_t* size, int G, in
 /* --------------------------------------------------------- device layers */
 
 /* Describe a packed layer already resident in device memory.
- *   K, N        in/out features; K % 128 == 0, N % 64 == 0, both > 0
+ *   K, N        in/out features; K % 128 == 0, N % 16 == 0, both > 0 (else
+ *               INVALID_ARG).  Every entry point serves N % 16 == 0; the
+ *               64-column decode tiles (EXQ_VARIANT_DECODE64, decode plans)
+ *               need N % 64 == 0 and report UNSUPPORTED otherwise.
  *   widths_host host, uint8 [K/128]; copied, the caller may free it
  *   d_qweight   device, 16-byte aligned EXQ1 words (borrowed: must outlive the handle)
  *   d_scales    device, 16-byte aligned fp16 [G][N] (borrowed)
@@ -192,11 +195,14 @@ void exq_layer_destroy(exq_layer_t layer);
 /* y = x * W_hat^T on `stream`.
  *   x  device, fp16 [M][K] row-major, 16-byte aligned
  *   y  device, fp16 [M][N] row-major, 16-byte aligned, must not overlap x
- *   M >= 1.  By default M <= 64 uses the decode kernel (scale factored per
- *   group, MFMA accumulation; one launch per 16 rows) and larger M the
- *   prefill kernel (W_hat decoded exactly into fp16 MFMA operands,
+ *   M >= 1.  By default M <= 64 uses the decode kernel (each weight's
+ *   (c - z) formed exactly in fp16 before the MFMA multiply-accumulate, the
+ *   scale applied per group in fp32; one launch per 16 rows) and larger M
+ *   the prefill kernel (W_hat decoded exactly into fp16 MFMA operands,
  *   activation tiles in LDS); exq_autotune / exq_set_variant can change the
  *   choice for M <= 64.  Accumulation is fp32 in both; output is fp16 RNE.
+ *   A weight whose code is the zero point contributes an exact zero on
+ *   every path, whatever its activation.
  * Accuracy: |y - y_ref| <= 2e-3 * sum_k |x_k * w_hat_k| + 1e-5 per output,
  * y_ref the exact (fp64) product of the fp16 inputs. */
 exq_status exq_gemm(const void* x, int M, exq_layer_t layer, void* y, void* stream);
@@ -253,7 +259,8 @@ double exq_trimmed_mean(const float* samples, int n);
  * y ends up holding that choice's result.  Synchronizes with `stream`.
  *   choice_out    host int or NULL: the chosen EXQ_VARIANT_*
  *   times_us_out  host float [2] (M <= 16) or [3] (M > 16) or NULL: the trimmed
- *                 means in microseconds, in variant order from DECODE16
+ *                 means in microseconds, in variant order from DECODE16; -1
+ *                 for DECODE64 when N % 64 != 0 (not a candidate then)
  * Not to be run while other work uses the layer at the same M.  Errors:
  * INVALID_ARG (NULL, M outside 1..64, warmup < 0, reps outside 1..100000,
  * misaligned or overlapping x/y), HIP, or a launch's own error. */
@@ -261,7 +268,8 @@ exq_status exq_autotune(const void* x, int M, exq_layer_t layer, void* y, void* 
                         int* choice_out, float* times_us_out);
 
 /* Set the choice for (layer, M) directly (EXQ_VARIANT_DEFAULT restores the rule).
- * Errors: INVALID_ARG (NULL, M outside 1..64, unknown variant, PREFILL at M <= 16). */
+ * Errors: INVALID_ARG (NULL, M outside 1..64, unknown variant, PREFILL at M <= 16),
+ * UNSUPPORTED (DECODE64 for a layer with N % 64 != 0). */
 exq_status exq_set_variant(exq_layer_t layer, int M, int variant);
 
 /* Materialize W_hat^T: w_out device, fp16 [K][N] row-major (w_out[k*N + n]),
@@ -285,8 +293,10 @@ exq_status exq_dequant(exq_layer_t layer, void* w_out, void* stream);
  * x_i * W_i^T in one kernel launch, deterministically and to the same
  * accuracy bound as exq_gemm (its tiling, hence its summation order, may
  * differ from a single exq_gemm call).
- * Outputs must not overlap any input or each other.  Errors: INVALID_ARG,
- * UNSUPPORTED (more than 65535 linears or tiles of one linear), OOM, HIP. */
+ * Outputs must not overlap any input or each other.  Every argument of every
+ * entry is checked before the first quantized-scale expansion of a prefill
+ * plan is made.  Errors: INVALID_ARG, UNSUPPORTED (more than 65535 linears or
+ * tiles of one linear; a decode plan entry with N % 64 != 0), OOM, HIP. */
 exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* const* xs,
                            const void* const* ys, int M, exq_plan_t* out);
 exq_status exq_plan_run(exq_plan_t plan, void* stream);

@@ -12,13 +12,15 @@
 //     contiguous 256-byte runs;
 //   * a code field is masked in place into the low bits of an fp16 half,
 //     which then *is* the fp16 value c * 2^(o-24) (a subnormal): one AND per
-//     two weights, no conversion and no zero-point subtraction per weight;
+//     two weights, no conversion; one packed fp16 add of -z * 2^(o-24) then
+//     gives (c - z) * 2^(o-24) exactly (every operand and the result are
+//     multiples of 2^-24 below 2^-14), so a weight whose code is the zero
+//     point contributes an exact zero whatever its activation;
 //   * the multiply-accumulate runs on the matrix cores with
 //     v_mfma_f32_4x4x4_16b_f16; each 16-lane quarter is a set of four 4x4
-//     blocks that shares one activation block (cbsz = 2), read from LDS;
-//   * per group the per-offset partial sums are rescaled by 2^(24-o), the
-//     zero point is removed once with the quarter's activation sum and the
-//     fp16 scale is applied in fp32:  y += s * (sum x*c - 2^(b-1) * sum x);
+//     blocks that shares one activation block (cbsz = 2);
+//   * per group the per-offset partial sums are rescaled by 2^(24-o) and
+//     the fp16 scale is applied in fp32:  y += s * sum x * (c - z);
 //   * quarters and waves are reduced in a fixed order: no atomics, the result
 //     is deterministic.
 #include <hip/hip_runtime.h>
@@ -114,32 +116,16 @@ __device__ __forceinline__ u4v load_act(const LinearDev& L, const DecodeCtx& c, 
     return *gptr<u4v>(L.x + off);
 }
 
-// Sum of the activations a lane's column sees in this group (TC = 64: the
-// whole group; TC = 16: its quarter), for row 4rb + r: the 8 values of each
-// operand lane are summed with dot2 against ones, then the lanes holding the
-// same row are combined by xor-shuffles in a fixed order.  Every lane ends
-// with the sum for row (its lane % 4); the row-r value is then broadcast.
-
-template <int TC>
-__device__ __forceinline__ float act_sum_lane(const u4v X) {
-    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    float v = __builtin_amdgcn_fdot2(as_h2(X[0]), one, 0.0f, false);
-    v = __builtin_amdgcn_fdot2(as_h2(X[1]), one, v, false);
-    v = __builtin_amdgcn_fdot2(as_h2(X[2]), one, v, false);
-    v = __builtin_amdgcn_fdot2(as_h2(X[3]), one, v, false);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    if constexpr (TC == 64) {
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-    }
-    return v;
-}
-
-template <int TC>
-__device__ __forceinline__ float act_sum_row(float lane_sum, const DecodeCtx& c, int r) {
-    if constexpr (TC == 64) return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), r));
-    else return __shfl(lane_sum, 16 * c.q + r);
+// (c - z) * 2^(o-24) in both fp16 halves of a masked decoder-unit dword
+// holding c * 2^(o-24) (o = p0 * t, the unit's bit offset in its half):
+// one packed add of -z * 2^(o-24).  z << o < 2^10 for every width and
+// offset, so both operands and the sum are fp16 subnormals (or zero) on the
+// 2^-24 grid and the add is exact; c = z gives +0.
+template <int B, int O>
+__device__ __forceinline__ uint32_t unbias(uint32_t v) {
+    static_assert(((1u << (B - 1)) << O) < 1024u, "zero point must stay subnormal");
+    constexpr uint32_t zb = 0x8000u | ((1u << (B - 1)) << O);
+    return __builtin_bit_cast(uint32_t, as_h2(v) + as_h2(zb | (zb << 16)));
 }
 
 template <int B, int MB, int TC, bool M1, bool QS>
@@ -157,7 +143,7 @@ __device__ __forceinline__ void group_compute(const DecodeCtx& c, const uint32_t
         constexpr int t = U % C;
         uint32_t b0, b1;
         unit_pair<B, U, TT::NQ>(Q, b0, b1);
-        const h4 bv = as_h4(b0, b1);
+        const h4 bv = as_h4(unbias<B, Width<B>::p0 * t>(b0), unbias<B, Width<B>::p0 * t>(b1));
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) {
             const h4 av = (U & 1) ? as_h4(X[rb][2], X[rb][3]) : as_h4(X[rb][0], X[rb][1]);
@@ -165,17 +151,14 @@ __device__ __forceinline__ void group_compute(const DecodeCtx& c, const uint32_t
         }
     });
     const float s = group_scale<B, QS>(c.ref, c.n, s16);
-    constexpr float z = (float)(1 << (B - 1));
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
-        const float xl = act_sum_lane<TC>(X[rb]);
 #pragma unroll
         for (int r = 0; r < (M1 ? 1 : 4); ++r) {
             if (M1 || 4 * rb + r < c.M) {
                 float tv = acc[0][rb][r] * class_factor<B>(0);
 #pragma unroll
                 for (int t = 1; t < C; ++t) tv = __builtin_fmaf(acc[t][rb][r], class_factor<B>(t), tv);
-                tv = __builtin_fmaf(-z, act_sum_row<TC>(xl, c, r), tv);
                 yacc[rb][r] = __builtin_fmaf(s, tv, yacc[rb][r]);
             }
         }
@@ -202,23 +185,22 @@ template <int MB, int TC> struct Rows {
 // x[r][128g + 32j + 8kk .. +8].  Lane (j, c) ends with rows 4j .. 4j + 3 of
 // its four columns.  Unit 2kk + 1 sits p0 bits above unit 2kk (the next
 // class); one shift puts both in unit 2kk's class, so each MFMA adds to one
-// class sum.  A fifth MFMA per K-step against all-z operands gives
-// z * sum_k x[r][k], the zero-point term, once for all columns.
+// class sum.  The zero point is removed from every weight (unbias) before
+// its MFMA.
 template <int B, bool QS>
 __device__ __forceinline__ void group_compute_mma(const DecodeCtx& c, const uint32_t (&Q)[4 * B], const u4v (&X)[4],
                                                   const uint16_t (&S)[4], float (&yacc)[4][4]) {
     using T = Width<B>;
     constexpr int NCLS = T::per == 4 ? 2 : 1;   // classes 0 and 2 for 2- and 3-bit groups, else 0
-    f4 acc[4][NCLS], accz = f4{0.f, 0.f, 0.f, 0.f};
+    f4 acc[4][NCLS];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int k = 0; k < NCLS; ++k) acc[cb][k] = f4{0.f, 0.f, 0.f, 0.f};
-    constexpr uint32_t zh = (uint32_t)(15 + B - 1) << 10;   // fp16 bits of z = 2^(B-1)
-    const h8 zop = __builtin_bit_cast(h8, u4v{zh | (zh << 16), zh | (zh << 16), zh | (zh << 16), zh | (zh << 16)});
     static_for<0, 4>([&](auto KC) {
         constexpr int kk = decltype(KC)::value;
         constexpr int cls = NCLS == 2 ? (kk & 1) : 0;
+        constexpr int O = T::p0 * ((2 * kk) % T::per);   // bit offset of unit 2kk (and, shifted, 2kk + 1)
         const h8 xop = __builtin_bit_cast(h8, X[kk]);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
@@ -229,10 +211,10 @@ __device__ __forceinline__ void group_compute_mma(const DecodeCtx& c, const uint
                 b0 >>= T::p0;
                 b1 >>= T::p0;
             }
-            const h8 wop = __builtin_bit_cast(h8, u4v{a0, a1, b0, b1});
+            const h8 wop = __builtin_bit_cast(
+                h8, u4v{unbias<B, O>(a0), unbias<B, O>(a1), unbias<B, O>(b0), unbias<B, O>(b1)});
             acc[cb][cls] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, wop, acc[cb][cls], 0, 0, 0);
         }
-        accz = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, zop, accz, 0, 0, 0);
     });
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
@@ -241,7 +223,7 @@ __device__ __forceinline__ void group_compute_mma(const DecodeCtx& c, const uint
         for (int i = 0; i < 4; ++i) {
             float tv = acc[cb][0][i] * class_factor<B>(0);
             if constexpr (NCLS == 2) tv = __builtin_fmaf(acc[cb][1][i], class_factor<B>(2), tv);
-            yacc[cb][i] = __builtin_fmaf(s, tv - accz[i], yacc[cb][i]);
+            yacc[cb][i] = __builtin_fmaf(s, tv, yacc[cb][i]);
         }
     }
 }
@@ -628,7 +610,11 @@ namespace {
 // wider tile's shared activation loads pay for the emptier machine: measured
 // 1.2x at 4 rows and 1.6x at 16 on 8192 columns); else 16.
 // 64 columns for wide layers, and always above 4 rows (the 16-row MFMA layout).
-int tile_cols_for(int N, int m) { return (m > 4 || N / 64 >= 256 || (m >= 4 && N / 64 >= 128)) ? 64 : 16; }
+// N not a multiple of 64: 16 always.
+int tile_cols_for(int N, int m) {
+    if (N % 64) return 16;
+    return (m > 4 || N / 64 >= 256 || (m >= 4 && N / 64 >= 128)) ? 64 : 16;
+}
 
 template <int MB, int TC, bool M1>
 void launch_decode_t(LinearDev d, int M, hipStream_t stream) {
@@ -721,6 +707,8 @@ exq_status exq_decode_rows(const exq_layer* L, const void* x, int M, void* y, hi
             exq_status st = launch_decode(d, m, stream);
             if (st != EXQ_OK) return st;
         } else {
+            if (tc == 64 && L->N % 64)
+                return fail(EXQ_ERR_UNSUPPORTED, "64-column decode tiles need N %% 64 == 0 (N=%d)", L->N);
             if (tc == 64) launch_decode_mb<64>(d, m, stream);
             else launch_decode_mb<16>(d, m, stream);
             hipError_t e = hipGetLastError();
@@ -785,7 +773,7 @@ static exq_status layer_create(int K, int N, int group_size, const uint8_t* widt
     *out = nullptr;
     exq_status st = check_layer_shape(K, N, group_size, widths_host);
     if (st != EXQ_OK) return st;
-    if (N % 64) return fail(EXQ_ERR_INVALID_ARG, "N=%d is not a multiple of 64", N);
+    if (N % 16) return fail(EXQ_ERR_INVALID_ARG, "N=%d is not a multiple of 16", N);
     const bool qs = d_scales == nullptr;
     if (!d_qweight || (!qs && !d_scales) || (qs && (!d_qscale || !d_ref)))
         return fail(EXQ_ERR_INVALID_ARG, "NULL device buffer");
@@ -876,6 +864,8 @@ exq_status exq_set_variant(exq_layer_t L, int M, int variant) {
     if (variant < 0 || variant >= kNumVariants) return fail(EXQ_ERR_INVALID_ARG, "variant %d", variant);
     if (variant == kVarPrefill && M <= kMaxDecodeM)
         return fail(EXQ_ERR_INVALID_ARG, "the prefill kernel serves M > %d", kMaxDecodeM);
+    if (variant == kVarDecode64 && L->N % 64)
+        return fail(EXQ_ERR_UNSUPPORTED, "64-column decode tiles need N %% 64 == 0 (N=%d)", L->N);
     L->tuned[M].store((uint8_t)variant, std::memory_order_relaxed);
     return EXQ_OK;
 }
@@ -906,6 +896,10 @@ exq_status exq_autotune(const void* x, int M, exq_layer_t L, void* y, void* stre
     int best = kVarDefault;
     double best_t = 0.0;
     for (int v = first; v <= last; ++v) {
+        if (v == kVarDecode64 && L->N % 64) {   // not served: no time
+            if (times_us_out) times_us_out[v - first] = -1.0f;
+            continue;
+        }
         exq_status st = EXQ_OK;
         for (int i = 0; i < warmup && st == EXQ_OK; ++i) st = run_variant(L, x, M, y, s, v);
         for (int i = 0; i < reps && st == EXQ_OK; ++i) {
@@ -1014,6 +1008,7 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
         if (!layers[i] || !xs[i] || !ys[i]) return fail(EXQ_ERR_INVALID_ARG, "plan entry %d is NULL", i);
     std::vector<LinearDev> list(count);
     std::vector<int> work(count);
+    long total_tiles = 0;
     for (int i = 0; i < count; ++i) {
         const exq_layer* L = layers[i];
         if (!aligned16(xs[i]) || !aligned16(ys[i])) return fail(EXQ_ERR_INVALID_ARG, "plan entry %d misaligned", i);
@@ -1023,16 +1018,31 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
             if (j != i && overlap(ys[i], 2 * (size_t)M * L->N, ys[j], 2 * (size_t)M * layers[j]->N))
                 return fail(EXQ_ERR_INVALID_ARG, "outputs %d and %d overlap", i, j);
         }
-        if (prefill) {
-            exq_status st = ensure_scales(layers[i], nullptr);
-            if (st != EXQ_OK) return st;
-        }
-        list[i] = linear_dev(L, xs[i], const_cast<void*>(ys[i]));
         if (!prefill && L->qs != layers[0]->qs)
             return fail(EXQ_ERR_INVALID_ARG, "a decode plan needs one scale storage for all linears (entry %d differs)", i);
         if (prefill) {
+            if (exq_prefill_tiles(L, M) == 0)
+                return fail(EXQ_ERR_UNSUPPORTED, "entry %d: K or M too large for a prefill plan", i);
+        } else if (L->N % 64) {
+            return fail(EXQ_ERR_UNSUPPORTED, "entry %d: decode plans use 64-column tiles, N=%d", i, L->N);
+        } else if (L->N / 64 >= 65536) {
+            return fail(EXQ_ERR_UNSUPPORTED, "entry %d has too many tiles", i);
+        }
+        total_tiles += prefill ? exq_prefill_tiles(L, M) : L->N / 64;
+    }
+    // A prefill map is padded to 8 equal XCD queues: at most 8x the tiles.
+    if (total_tiles > (long)(INT32_MAX / kXcds)) return fail(EXQ_ERR_UNSUPPORTED, "plan too large");
+    // Every argument is valid: only now expand quantized scales (a prefill
+    // plan's kernels read fp16 scales), so a failed call launches nothing.
+    for (int i = 0; i < count && prefill; ++i) {
+        exq_status st = ensure_scales(layers[i], nullptr);
+        if (st != EXQ_OK) return st;
+    }
+    for (int i = 0; i < count; ++i) {
+        const exq_layer* L = layers[i];
+        list[i] = linear_dev(L, xs[i], const_cast<void*>(ys[i]));
+        if (prefill) {
             list[i].tiles = exq_prefill_tiles(L, M);
-            if (list[i].tiles == 0) return fail(EXQ_ERR_UNSUPPORTED, "entry %d: K or M too large for a prefill plan", i);
             work[i] = L->K;   // per-workgroup cost: one tile over all of K
         } else {
             list[i].tiles = L->N / 64;
@@ -1079,9 +1089,6 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
         for (size_t k = 0; k < longest; ++k)
             for (int x = 0; x < kXcds; ++x) wg_map.push_back(k < queue[x].size() ? queue[x][k] : kPlanEmpty);
     }
-    if (wg_map.size() > (size_t)INT32_MAX) return fail(EXQ_ERR_UNSUPPORTED, "plan too large");
-    for (int i = 0; i < count; ++i)
-        if (list[i].tiles >= 65536) return fail(EXQ_ERR_UNSUPPORTED, "entry %d has too many tiles", i);
     exq_plan* P = new (std::nothrow) exq_plan();
     if (!P) return fail(EXQ_ERR_OOM, "host allocation");
     P->count = count;

@@ -70,7 +70,7 @@ def test_pack_rejects_bad_input():
 def test_layer_and_gemm_validation_before_any_launch():
     w = np.array([4, 4], dtype=np.uint8)
     fake = 0x10000  # never dereferenced: every case fails validation first
-    _expect(exq.EXQ_ERR_INVALID_ARG, exq.exq_layer_create, 256, 96, w, fake, fake)      # N % 64
+    _expect(exq.EXQ_ERR_INVALID_ARG, exq.exq_layer_create, 256, 72, w, fake, fake)      # N % 16
     _expect(exq.EXQ_ERR_INVALID_ARG, exq.exq_layer_create, 200, 64, w, fake, fake)      # K % 128
     _expect(exq.EXQ_ERR_UNSUPPORTED, exq.exq_layer_create, 256, 64, [4, 4, 4, 4], fake, fake, 64)
     _expect(exq.EXQ_ERR_INVALID_ARG, exq.exq_layer_create, 256, 64, [4, 7], fake, fake)
@@ -175,3 +175,15 @@ int main() {
     exe = tmp_path / "xcd_blocks"
     subprocess.run([cxx, "-std=c++17", "-O1", "-o", str(exe), str(src)], check=True)
     assert subprocess.run([str(exe)]).returncode == 0
+
+
+def test_layer_create_accepts_n_multiple_of_16():
+    """N = 80 and 96 pass validation (a multiple of 16 is served); without a GPU
+    the metadata allocation is what fails, never argument validation."""
+    w = np.array([4, 4], dtype=np.uint8)
+    for N in (80, 96, 16):
+        h = ctypes.c_void_p()
+        st = exq.lib.exq_layer_create(256, N, 128, w.ctypes.data, 0x10000, 0x10000, ctypes.byref(h))
+        assert st in (exq.EXQ_OK, exq.EXQ_ERR_OOM, exq.EXQ_ERR_HIP), (N, st)
+        if st == exq.EXQ_OK:
+            exq.exq_layer_destroy(h.value)

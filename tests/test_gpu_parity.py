@@ -312,3 +312,106 @@ def test_plan_rejects_bad_arguments(exq):
         exq.exq_plan_destroy(exq.exq_plan_create(handles, [x0, x0], [y0, y1], M))
     a.close()
     b.close()
+
+
+def test_plan_validates_every_entry_before_expanding_scales(exq):
+    """A prefill plan whose first entry has quantized scales and whose second
+    entry is invalid fails with INVALID_ARG before the first entry's fp16
+    scales are expanded (an 8 MiB device allocation and a kernel launch).
+    The device's free memory shows the expansion: a valid plan over the same
+    layer allocates it (the control), the failed one does not."""
+    G, N, M = 64, 65536, 20
+    K = 128 * G
+    widths = np.full(G, 2, dtype=np.uint8)
+    q = torch.zeros(exq.exq_packed_bytes(K, N, widths), dtype=torch.uint8, device="cuda")
+    qs = torch.zeros(G * N // 2, dtype=torch.uint8, device="cuda")
+    ref = torch.zeros(N, dtype=torch.int16, device="cuda")
+    W = synth.weight(synth.seed_for("plan-err-2"), 128, 256)
+    a, *_ = make_layer(exq, W, [3, 5])
+    big = [exq.exq_layer_create_qs(K, N, widths, q.data_ptr(), qs.data_ptr(), ref.data_ptr()) for _ in range(2)]
+    xb = torch.zeros((M, K), dtype=torch.float16, device="cuda")
+    yb = torch.zeros((M, N), dtype=torch.float16, device="cuda")
+    xa = torch.zeros((M, 256), dtype=torch.float16, device="cuda")
+    ya = torch.zeros((M, 128), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    expansion = 2 * G * N
+    try:
+        note("plan validation order: control")
+        free0 = torch.cuda.mem_get_info()[0]
+        exq.exq_plan_destroy(exq.exq_plan_create([big[0], a.handle], [xb.data_ptr(), xa.data_ptr()],
+                                                 [yb.data_ptr(), ya.data_ptr()], M))
+        torch.cuda.synchronize()
+        free1 = torch.cuda.mem_get_info()[0]
+        if free0 - free1 < expansion:
+            pytest.skip("the device's free-memory counter does not show an %d-byte allocation" % expansion)
+        note("plan validation order: misaligned second entry")
+        with pytest.raises(exq.ExqError) as ei:
+            exq.exq_plan_create([big[1], a.handle], [xb.data_ptr(), xa.data_ptr() + 2],
+                                [yb.data_ptr(), ya.data_ptr()], M)
+        assert ei.value.status == exq.EXQ_ERR_INVALID_ARG
+        torch.cuda.synchronize()
+        free2 = torch.cuda.mem_get_info()[0]
+        assert free1 - free2 < expansion, "the failed call allocated %d bytes" % (free1 - free2)
+    finally:
+        for h in big:
+            exq.exq_layer_destroy(h)
+        a.close()
+
+
+def test_n_multiple_of_16(exq):
+    """N = 80 (a multiple of 16, not of 64): decode (16-column tiles), prefill,
+    gated and dequant match the oracle; the 64-column choices report
+    UNSUPPORTED; prefill plans take it, decode plans refuse it."""
+    K, N = 640, 80
+    widths = [2, 8, 3, 6, 5]
+    W = synth.weight(synth.seed_for("n80"), N, K)
+    layer, codes, s_ref, q_ref = make_layer(exq, W, widths)
+    w_ref = oracle.dequant(codes, s_ref, widths)
+    try:
+        note("N=80 dequant")
+        np.testing.assert_array_equal(layer.dequant().cpu().numpy().view(np.uint16), w_ref)
+        for M in (1, 4, 5, 16, 33, 300):
+            x = synth.activations(synth.seed_for("n80-x", M), M, K)
+            note("N=80 gemm M=%d" % M)
+            y = y_to_np(layer.gemm(to_dev(x)))
+            y_ref, bnd = oracle.gemm(x, w_ref)
+            assert_within(y, y_ref, bnd, "N=80 M=%d" % M)
+        with pytest.raises(exq.ExqError) as ei:
+            exq.exq_set_variant(layer.handle, 4, exq.VARIANT_DECODE64)
+        assert ei.value.status == exq.EXQ_ERR_UNSUPPORTED
+        x = to_dev(synth.activations(synth.seed_for("n80-tune"), 4, K))
+        y = torch.empty((4, N), dtype=torch.float16, device="cuda")
+        note("N=80 autotune M=4")
+        choice, times = exq.exq_autotune(x.data_ptr(), 4, layer.handle, y.data_ptr(), None, 2, 5)
+        assert choice == exq.VARIANT_DECODE16 and times[1] == -1.0
+        exq.exq_set_variant(layer.handle, 4, exq.VARIANT_DEFAULT)
+        # gated pair of N = 80
+        W2 = synth.weight(synth.seed_for("n80-up"), N, K)
+        up, c2, s2, _ = make_layer(exq, W2, widths)
+        w2 = oracle.dequant(c2, s2, widths)
+        for M in (1, 16, 300):
+            x = synth.activations(synth.seed_for("n80-g", M), M, K)
+            note("N=80 gated M=%d" % M)
+            h = y_to_np(exq.gemm_gated(to_dev(x), layer, up))
+            h_ref, allow = oracle.gated(x, w_ref, w2)
+            ok, worst = oracle.within_allowance(h, h_ref, allow)
+            assert ok, "N=80 gated M=%d: %.3f" % (M, worst)
+        # plans
+        for M, ok_expected in ((1, False), (16, False), (40, True)):
+            xs = [to_dev(synth.activations(synth.seed_for("n80-p", M, i), M, K)) for i in range(2)]
+            ys = [torch.empty((M, N), dtype=torch.float16, device="cuda") for _ in range(2)]
+            if not ok_expected:
+                with pytest.raises(exq.ExqError) as ei:
+                    exq.Plan([layer, up], xs, ys, M)
+                assert ei.value.status == exq.EXQ_ERR_UNSUPPORTED
+                continue
+            note("N=80 prefill plan M=%d" % M)
+            p = exq.Plan([layer, up], xs, ys, M)
+            p.run()
+            for i, wr in enumerate((w_ref, w2)):
+                y_ref, bnd = oracle.gemm(xs[i].cpu().numpy(), wr)
+                assert_within(y_to_np(ys[i]), y_ref, bnd, "N=80 plan M=%d entry %d" % (M, i))
+            p.close()
+        up.close()
+    finally:
+        layer.close()

@@ -207,6 +207,21 @@ void exq_layer_destroy(exq_layer_t layer);
  * y_ref the exact (fp64) product of the fp16 inputs. */
 exq_status exq_gemm(const void* x, int M, exq_layer_t layer, void* y, void* stream);
 
+/* exq_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernel choice, results and errors as exq_gemm, and it calls no
+ * hipMalloc, hipFree, allocating library routine or synchronization.  The only
+ * call-time allocation of exq_gemm is the fp16 expansion of a quantized-scale
+ * layer's group scales for the prefill kernel (exq_layer_create_qs); here every
+ * call that needs it rewrites it, on `stream`, into a static device array of
+ * 16 MiB (one per device, held until the process ends) and the prefill kernel
+ * reads it there.  So 2*(K/128)*N must not exceed 16 MiB (else UNSUPPORTED,
+ * before any launch).  Every call on one device shares that array: calls that
+ * overlap on one device (other streams, or host threads) race and must be
+ * ordered by the caller.  The first call on a device looks up the array's
+ * device address (hipGetSymbolAddress, no allocation). */
+exq_status exq_gemm_noalloc(const void* x, int M, exq_layer_t layer, void* y, void* stream);
+
 /* h = SiLU(x * Wg_hat^T) (.) (x * Wu_hat^T), SiLU(t) = t / (1 + e^-t): a gate
  * and an up linear that share their input, fused with the activation between
  * them.  (The exllamav3 article, section "technical deep dive", fuses

@@ -56,6 +56,7 @@ def _load():
     lib.exq_layer_destroy.argtypes = [vp]
     lib.exq_layer_destroy.restype = None
     lib.exq_gemm.argtypes = [vp, i32, vp, vp, vp]
+    lib.exq_gemm_noalloc.argtypes = [vp, i32, vp, vp, vp]
     lib.exq_dequant.argtypes = [vp, vp, vp]
     lib.exq_plan_create.argtypes = [i32, vp, vp, vp, i32, ctypes.POINTER(vp)]
     lib.exq_plan_run.argtypes = [vp, vp]
@@ -71,7 +72,7 @@ def _load():
     lib.exq_autotune.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp]
     lib.exq_set_variant.argtypes = [vp, i32, i32]
     lib.exq_allocate_widths.argtypes = [vp, vp, i32, ctypes.c_int64, vp, ctypes.c_uint64, ctypes.c_int64, vp, vp]
-    for f in (lib.exq_pack, lib.exq_layer_create, lib.exq_gemm, lib.exq_dequant, lib.exq_plan_create,
+    for f in (lib.exq_pack, lib.exq_layer_create, lib.exq_gemm, lib.exq_gemm_noalloc, lib.exq_dequant, lib.exq_plan_create,
               lib.exq_plan_run, lib.exq_stream_read, lib.exq_gemm_gated, lib.exq_group_errors,
               lib.exq_allocate_widths, lib.exq_autotune, lib.exq_set_variant, lib.exq_pack_qs,
               lib.exq_layer_create_qs):
@@ -86,7 +87,7 @@ EXPORTED = (
     "exq_status_string", "exq_last_error", "exq_packed_bytes", "exq_pack", "exq_layer_create",
     "exq_layer_destroy", "exq_gemm", "exq_dequant", "exq_plan_create", "exq_plan_run", "exq_plan_destroy",
     "exq_stream_read", "exq_gemm_gated", "exq_group_errors", "exq_allocate_widths", "exq_trimmed_mean",
-    "exq_autotune", "exq_set_variant", "exq_pack_qs", "exq_layer_create_qs",
+    "exq_autotune", "exq_set_variant", "exq_pack_qs", "exq_layer_create_qs", "exq_gemm_noalloc",
 )
 
 VARIANT_DEFAULT, VARIANT_DECODE16, VARIANT_DECODE64, VARIANT_PREFILL = 0, 1, 2, 3
@@ -180,6 +181,10 @@ def exq_layer_destroy(handle: int) -> None:
 
 def exq_gemm(x_ptr: int, M: int, handle: int, y_ptr: int, stream=None) -> None:
     _check(lib.exq_gemm(x_ptr, M, handle, y_ptr, _stream_ptr(stream)), "exq_gemm")
+
+
+def exq_gemm_noalloc(x_ptr: int, M: int, handle: int, y_ptr: int, stream=None) -> None:
+    _check(lib.exq_gemm_noalloc(x_ptr, M, handle, y_ptr, _stream_ptr(stream)), "exq_gemm_noalloc")
 
 
 def exq_gemm_gated(x_ptr: int, M: int, gate: int, up: int, h_ptr: int, stream=None) -> None:

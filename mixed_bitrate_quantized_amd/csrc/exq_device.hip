@@ -462,6 +462,14 @@ __global__ __launch_bounds__(256) void expand_qs_kernel(const uint8_t* __restric
     *gptr_w<uint16_t>(out + i) = __builtin_bit_cast(uint16_t, (_Float16)u);
 }
 
+// ------------------------------------------------ allocation-free scratch
+
+// Device scratch of exq_gemm_noalloc: the fp16 expansion of a quantized-scale
+// layer's group scales, remade by every call that needs it.  Each device the
+// library runs on holds its own copy until the process ends.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 // ---------------------------------------------------------------- dequant
 
 // One lane per (column, quarter): decodes its 32 codes of group g and writes
@@ -691,12 +699,43 @@ void launch_plan(const exq_plan* P, hipStream_t s) {
 
 extern exq_status exq_prefill_launch(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream);
 extern exq_status exq_prefill_launch_gated(const exq_layer* U, const void* x, int M, void* h, hipStream_t stream);
+extern exq_status exq_prefill_launch_desc(const LinearDev& d, int M, hipStream_t stream);
 extern int exq_prefill_tiles(const exq_layer* L, int M);
 extern exq_status exq_prefill_plan_launch(const LinearDev* d_list, const uint32_t* d_wg_map, int total_wgs, int M,
                                           hipStream_t stream);
 
 // Decode kernel over consecutive slices of at most 16 rows of x (any M);
 // tc = 0: the tile width of tile_cols_for, else 16 or 64.
+// The device address of `scratch` on the current device, looked up with
+// hipGetSymbolAddress on the first call per device and kept.  (The array's
+// name in host code is a host-side stand-in, never a device address.)
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+exq_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(EXQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(EXQ_ERR_UNSUPPORTED, "device %d (at most %d)", dev, kMaxDevices);
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_acquire);
+        if (!p) {
+            if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess || !p)
+                return fail(EXQ_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return EXQ_OK;
+}
+
+}  // namespace
+
 exq_status exq_decode_rows(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream, int tc = 0) {
     for (int r0 = 0; r0 < M; r0 += kMaxDecodeM) {
         const int m = std::min(kMaxDecodeM, M - r0);
@@ -856,6 +895,36 @@ exq_status exq_gemm(const void* x, int M, exq_layer_t L, void* y, void* stream) 
     if (overlap(x, 2 * (size_t)M * L->K, y, 2 * (size_t)M * L->N)) return fail(EXQ_ERR_INVALID_ARG, "y overlaps x");
     const int v = M <= kTuneMaxM ? L->tuned[M].load(std::memory_order_relaxed) : kVarDefault;
     return run_variant(L, x, M, y, static_cast<hipStream_t>(stream), v);
+}
+
+exq_status exq_gemm_noalloc(const void* x, int M, exq_layer_t L, void* y, void* stream) {
+    if (!L) return fail(EXQ_ERR_INVALID_ARG, "layer is NULL");
+    if (!x || !y) return fail(EXQ_ERR_INVALID_ARG, "NULL x or y");
+    if (M < 1) return fail(EXQ_ERR_INVALID_ARG, "M=%d must be >= 1", M);
+    if (!aligned16(x) || !aligned16(y)) return fail(EXQ_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    if (overlap(x, 2 * (size_t)M * L->K, y, 2 * (size_t)M * L->N)) return fail(EXQ_ERR_INVALID_ARG, "y overlaps x");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int v = M <= kTuneMaxM ? L->tuned[M].load(std::memory_order_relaxed) : kVarDefault;
+    const bool prefill = v == kVarPrefill || (v == kVarDefault && M > kTuneMaxM);
+    // Decode kernels read the 4-bit codes or the fp16 scales, and fp16-scale
+    // layers need nothing more: those launches allocate nothing already.
+    if (!prefill || !L->qs) return run_variant(L, x, M, y, s, v);
+    const size_t need = 2 * (size_t)L->G * (size_t)L->N;
+    if (need > kScratchBytes)
+        return fail(EXQ_ERR_UNSUPPORTED, "the fp16 scales of this layer (%zu bytes) exceed the %zu-byte scratch", need,
+                    kScratchBytes);
+    void* scr = nullptr;
+    exq_status st = scratch_address(&scr);
+    if (st != EXQ_OK) return st;
+    const size_t n = (size_t)L->G * L->N;
+    hipLaunchKernelGGL(expand_qs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(L->qscale), static_cast<const uint16_t*>(L->ref), L->d_meta, L->G,
+                       L->N, static_cast<uint16_t*>(scr));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "scale expansion launch");
+    LinearDev d = linear_dev(L, x, y);
+    d.scales = static_cast<const uint16_t*>(scr);
+    return exq_prefill_launch_desc(d, M, s);
 }
 
 exq_status exq_set_variant(exq_layer_t L, int M, int variant) {

@@ -489,13 +489,12 @@ using namespace exq;
 namespace {
 
 template <bool GATED>
-exq_status prefill_launch(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream) {
+exq_status prefill_launch_dev(const LinearDev& d, int M, hipStream_t stream) {
     // Offsets into one tile's rows of x are 32-bit: 2 * 256 * K bytes must stay below 2^31.
-    if ((size_t)2 * kPT * (size_t)L->K >= (size_t)kBufOOB)
-        return fail(EXQ_ERR_UNSUPPORTED, "K=%d is too large for the prefill kernel", L->K);
-    const long row_tiles = (M + kPT - 1) / kPT, col_tiles = (L->N + kPT - 1) / kPT;
+    if ((size_t)2 * kPT * (size_t)d.K >= (size_t)kBufOOB)
+        return fail(EXQ_ERR_UNSUPPORTED, "K=%d is too large for the prefill kernel", d.K);
+    const long row_tiles = (M + kPT - 1) / kPT, col_tiles = (d.N + kPT - 1) / kPT;
     if (row_tiles * col_tiles > INT_MAX) return fail(EXQ_ERR_UNSUPPORTED, "M=%d gives too many tiles", M);
-    LinearDev d = linear_dev(L, x, y);
     long per_xcd = 0;   // the largest block: 8 of them cover every tile
     for (int blk = 0; blk < 8; ++blk) {
         const XcdBlock b = xcd_block((int)row_tiles, (int)col_tiles, blk);
@@ -510,12 +509,17 @@ exq_status prefill_launch(const exq_layer* L, const void* x, int M, void* y, hip
 }  // namespace
 
 exq_status exq_prefill_launch(const exq_layer* L, const void* x, int M, void* y, hipStream_t stream) {
-    return prefill_launch<false>(L, x, M, y, stream);
+    return prefill_launch_dev<false>(linear_dev(L, x, y), M, stream);
+}
+
+// A descriptor whose fp16 scales the caller provides (the allocation-free entry point).
+exq_status exq_prefill_launch_desc(const LinearDev& d, int M, hipStream_t stream) {
+    return prefill_launch_dev<false>(d, M, stream);
 }
 
 // h holds the gate product; writes SiLU(h) * (x W_up^T) over it.
 exq_status exq_prefill_launch_gated(const exq_layer* U, const void* x, int M, void* h, hipStream_t stream) {
-    return prefill_launch<true>(U, x, M, h, stream);
+    return prefill_launch_dev<true>(linear_dev(U, x, h), M, stream);
 }
 
 // Tiles of one linear in a prefill plan (0 if the linear cannot be planned).

@@ -526,7 +526,9 @@ def back_to_back_leg(exq, torch, specs, layers, xs, ys, nblk, M, steps, stream, 
     for b in range(nblk):
         L = layers[b * per:(b + 1) * per]
         X = xs[b * per:(b + 1) * per]
-        Y = ys[b * per:(b + 1) * per]
+        # Own outputs: k, v and down here read other inputs than the stack's own
+        # x buffers, and the stack's outputs are checked against the oracle later.
+        Y = [torch.empty_like(y) for y in ys[b * per:(b + 1) * per]]
         h = torch.empty((M, L[ig].N), dtype=torch.float16, device="cuda")
         qkv = exq.Plan([L[iq], L[ik], L[iv]], [X[iq], X[iq], X[iq]], [Y[iq], Y[ik], Y[iv]], M)
         blocks.append((qkv, L, X, Y, h))

@@ -3,7 +3,7 @@
 //
 // Decode design (M <= 16, HBM-bound):
 //   * a workgroup owns 16 output columns over the whole of K; its 8 waves
-//     share the groups, pre-sorted by width and cut into byte-balanced
+//     share the groups, pre-sorted by width and cut into instruction-balanced
 //     chunks, so a wave streams one or two runs of equal-width groups and its
 //     software pipeline waits on compile-time load counts;
 //   * lane l handles column l % 16 and K-quarter q = l / 16 of every group:
@@ -569,6 +569,9 @@ struct exq_plan {
     bool qs = false;        // decode plan of layers with quantized scales
     LinearDev* d_list = nullptr;
     uint32_t* d_wg_map = nullptr;
+    uint32_t* d_part_map = nullptr;   // prefill: K-piece of each workgroup's tile
+    float* d_ws = nullptr;            // prefill: partial sums of tiles cut along K
+    uint32_t* d_counters = nullptr;   // prefill: arrivals at each cut tile (zero between launches)
 };
 
 namespace {
@@ -701,8 +704,8 @@ extern exq_status exq_prefill_launch(const exq_layer* L, const void* x, int M, v
 extern exq_status exq_prefill_launch_gated(const exq_layer* U, const void* x, int M, void* h, hipStream_t stream);
 extern exq_status exq_prefill_launch_desc(const LinearDev& d, int M, hipStream_t stream);
 extern int exq_prefill_tiles(const exq_layer* L, int M);
-extern exq_status exq_prefill_plan_launch(const LinearDev* d_list, const uint32_t* d_wg_map, int total_wgs, int M,
-                                          hipStream_t stream);
+extern exq_status exq_prefill_plan_launch(const LinearDev* d_list, const uint32_t* d_wg_map, const uint32_t* d_part_map,
+                                          float* d_ws, uint32_t* d_counters, int total_wgs, int M, hipStream_t stream);
 
 // Decode kernel over consecutive slices of at most 16 rows of x (any M);
 // tc = 0: the tile width of tile_cols_for, else 16 or 64.
@@ -1125,7 +1128,8 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
     std::vector<int> byw(count);
     for (int i = 0; i < count; ++i) byw[i] = i;
     std::stable_sort(byw.begin(), byw.end(), [&](int a, int b) { return work[a] > work[b]; });
-    std::vector<uint32_t> wg_map;
+    std::vector<uint32_t> wg_map, part_map;
+    uint32_t split_slots = 0;
     if (!prefill) {
         for (int i : byw)
             for (int t = 0; t < list[i].tiles; ++t) wg_map.push_back((uint32_t)i | ((uint32_t)t << 16));
@@ -1153,10 +1157,44 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
                 load[x] += (long)b.nr * b.nc * work[i];
             }
         }
+        // An XCD runs its queue on its compute units (one prefill workgroup
+        // each), in order.  When the tiles after its first round do not fill
+        // the last round, the tiles of that partial round are cut along K
+        // into up to kPlanParts pieces, so the pieces fill it.  (Measured on
+        // the 70B block at M = 2048: each XCD ran 32 long tiles, then 9
+        // rounds of 32 short ones and a last round of 8.)
+        int dev = 0, cus = 0;
+        hipError_t e;
+        if ((e = hipGetDevice(&dev)) != hipSuccess ||
+            (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+            return hip_fail(e, "compute unit count");
+        const int per_xcd = std::max(1, cus / kXcds);
+        std::vector<std::vector<uint32_t>> parts(kXcds);
+        for (int x = 0; x < kXcds; ++x) {
+            const int n = (int)queue[x].size();
+            const int r = n > per_xcd ? (n - per_xcd) % per_xcd : 0;
+            const int np = r > 0 ? std::min(kPlanParts, per_xcd / r) : 1;
+            std::vector<uint32_t> q2, p2;
+            for (int k = 0; k < n; ++k) {
+                const uint32_t ent = queue[x][k];
+                const int G = layers[ent & 0xFFFFu]->G;
+                const int pieces = (k >= n - r && np > 1 && G >= np) ? np : 1;
+                const uint32_t slot = pieces > 1 ? split_slots++ : 0u;
+                for (int pc = 0; pc < pieces; ++pc) {
+                    q2.push_back(ent);
+                    p2.push_back((uint32_t)pc | ((uint32_t)pieces << 4) | (slot << 8));
+                }
+            }
+            queue[x].swap(q2);
+            parts[x].swap(p2);
+        }
         size_t longest = 0;
         for (const auto& q : queue) longest = std::max(longest, q.size());
         for (size_t k = 0; k < longest; ++k)
-            for (int x = 0; x < kXcds; ++x) wg_map.push_back(k < queue[x].size() ? queue[x][k] : kPlanEmpty);
+            for (int x = 0; x < kXcds; ++x) {
+                wg_map.push_back(k < queue[x].size() ? queue[x][k] : kPlanEmpty);
+                part_map.push_back(k < queue[x].size() ? parts[x][k] : 1u << 4);
+            }
     }
     exq_plan* P = new (std::nothrow) exq_plan();
     if (!P) return fail(EXQ_ERR_OOM, "host allocation");
@@ -1177,13 +1215,32 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
         exq_plan_destroy(P);
         return hip_fail(e, "hipMemcpy plan");
     }
+    if (prefill) {
+        const size_t ws_floats = (size_t)std::max<uint32_t>(split_slots, 1) * kPlanParts * 256 * 256;
+        const size_t ncnt = std::max<uint32_t>(split_slots, 1);
+        if ((e = hipMalloc(&P->d_part_map, sizeof(uint32_t) * part_map.size())) != hipSuccess ||
+            (e = hipMalloc(&P->d_ws, sizeof(float) * ws_floats)) != hipSuccess ||
+            (e = hipMalloc(&P->d_counters, sizeof(uint32_t) * ncnt)) != hipSuccess) {
+            exq_plan_destroy(P);
+            return fail(EXQ_ERR_OOM, "hipMalloc plan");
+        }
+        if ((e = hipMemcpy(P->d_part_map, part_map.data(), sizeof(uint32_t) * part_map.size(),
+                           hipMemcpyHostToDevice)) != hipSuccess ||
+            (e = hipMemset(P->d_counters, 0, sizeof(uint32_t) * ncnt)) != hipSuccess ||
+            (e = hipDeviceSynchronize()) != hipSuccess) {
+            exq_plan_destroy(P);
+            return hip_fail(e, "hipMemcpy plan");
+        }
+    }
     *out = P;
     return EXQ_OK;
 }
 
 exq_status exq_plan_run(exq_plan_t P, void* stream) {
     if (!P) return fail(EXQ_ERR_INVALID_ARG, "plan is NULL");
-    if (P->prefill) return exq_prefill_plan_launch(P->d_list, P->d_wg_map, P->total_wgs, P->M, static_cast<hipStream_t>(stream));
+    if (P->prefill)
+        return exq_prefill_plan_launch(P->d_list, P->d_wg_map, P->d_part_map, P->d_ws, P->d_counters, P->total_wgs, P->M,
+                                       static_cast<hipStream_t>(stream));
     launch_plan(P, static_cast<hipStream_t>(stream));
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? EXQ_OK : hip_fail(e, "plan launch");
@@ -1193,6 +1250,9 @@ void exq_plan_destroy(exq_plan_t P) {
     if (!P) return;
     if (P->d_list) (void)hipFree(P->d_list);
     if (P->d_wg_map) (void)hipFree(P->d_wg_map);
+    if (P->d_part_map) (void)hipFree(P->d_part_map);
+    if (P->d_ws) (void)hipFree(P->d_ws);
+    if (P->d_counters) (void)hipFree(P->d_counters);
     delete P;
 }
 

@@ -121,10 +121,18 @@ WavePlan plan_waves(int K, const uint8_t* widths) {
     std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return widths[a] < widths[b]; });
     p.order.resize(G);
     for (int i = 0; i < G; ++i) p.order[i] = (uint32_t)idx[i] | (prefix[idx[i]] << 16);
-    // Byte-balanced cuts of the sorted list: a group costs b_g words per
-    // column plus a fixed share for its scale, activations and epilogue.
+    // Balanced cuts of the sorted list.  Decode is bound by instruction
+    // issue, so a group costs the instructions its decode issues per wave
+    // (masks, the exact zero-point subtracts, field merges of split widths,
+    // MFMAs): about 178, 258, 186, 272, 272 and 192 at widths 2, 3, 4, 5, 6, 8,
+    // counted in the 64-column kernel's code.  (Measured on the 70B block: a
+    // byte-balanced cut left the waves with the most 2- and 3-bit groups last
+    // in every workgroup, and the 16-row kernel ran 3.6 % slower.)
+    auto cost = [](int b) {
+        return b == 2 ? 178.0 : b == 3 ? 258.0 : b == 4 ? 186.0 : b == 8 ? 192.0 : 272.0;
+    };
     std::vector<double> cum(G + 1, 0.0);
-    for (int i = 0; i < G; ++i) cum[i + 1] = cum[i] + widths[idx[i]] + 1.0;
+    for (int i = 0; i < G; ++i) cum[i + 1] = cum[i] + cost(widths[idx[i]]);
     p.bounds.assign(kWaves + 1, 0);
     p.bounds[kWaves] = (uint16_t)G;
     int i = 0;

@@ -31,6 +31,10 @@ constexpr XcdBlock xcd_block(int row_tiles, int col_tiles, int b) {
     return XcdBlock{r0, r1 - r0, c0, c1 - c0};
 }
 
+// Most pieces a prefill plan cuts one tile into along K (to fill the last
+// round of an XCD's queue).
+constexpr int kPlanParts = 4;
+
 // Kernel choices of exq_gemm (a layer's tuned entry for M, 0 = the default rule).
 enum Variant : uint8_t { kVarDefault = 0, kVarDecode16 = 1, kVarDecode64 = 2, kVarPrefill = 3, kNumVariants = 4 };
 
@@ -43,9 +47,9 @@ bool width_supported(int b);
 exq_status check_layer_shape(int K, int N, int group_size, const uint8_t* widths);
 
 // How the kWaves waves of a decode workgroup share a layer's groups.  All
-// groups are sorted by (width, index) and cut into kWaves contiguous,
-// byte-balanced chunks, so each wave streams one or two runs of equal-width
-// groups with a fixed number of loads per group.
+// groups are sorted by (width, index) and cut into kWaves contiguous chunks
+// of balanced decode instruction counts, so each wave streams one or two runs
+// of equal-width groups with a fixed number of loads per group.
 //   order[i] = g | (P_g << 16) in that sorted order;
 //   bounds[w] .. bounds[w+1] is wave w's chunk of `order`;
 //   runs[w*6 + i] counts its groups of width kWidthOrder[i].

@@ -60,19 +60,20 @@ struct PrefillCtx {
 // one kc touch 16 distinct slot / row-parity pairs: no bank conflicts.
 __device__ __forceinline__ uint32_t xswz(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
 
-// Where stage st comes from: half h = st % 2 of group g = st / 2.  A stage
-// past the last one reloads the last (cache hits, never used): a uniform test
-// on it would split the stage into branches.  Stages -2 and -1 (run first
-// when the stage count is 2 mod 4) read stage 0's words with an out-of-range
-// scale offset: scale 0, so every weight they decode is a zero.
+// Where stage st of a tile's stage range [lo, hi) comes from: half h = st % 2
+// of group g = st / 2.  A stage past the last one reloads the last (cache
+// hits, never used): a uniform test on it would split the stage into
+// branches.  Stages lo - 2 and lo - 1 (run first when the range holds 2 mod 4
+// stages) read stage lo's words with an out-of-range scale offset: scale 0,
+// so every weight they decode is a zero.
 struct StageSrc {
     uint32_t g, P, h, so;   // so: byte offset of the group's scales (out of range: zeros)
     int b;
 };
 
-__device__ __forceinline__ StageSrc stage_src(const LinearDev& L, int st, int S) {
-    const uint32_t null_scale = st < 0 ? kBufOOB : 0u;
-    st = max(min(st, S - 1), 0);
+__device__ __forceinline__ StageSrc stage_src(const LinearDev& L, int st, int lo, int hi) {
+    const uint32_t null_scale = st < lo ? kBufOOB : 0u;
+    st = max(min(st, hi - 1), lo);
     StageSrc r;
     r.g = (uint32_t)(st >> 1);
     r.h = (uint32_t)(st & 1);
@@ -277,7 +278,7 @@ __device__ __forceinline__ void region_schedule() {
 // barrier, whose wait covers them: scalar loads return out of order, so
 // while one is outstanding every wait for an operand read would drain all.
 template <bool NEXT_SAME_GROUP>
-__device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx& c, int st, int S,
+__device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx& c, int st, int lo, int hi,
                                            const uint16_t* rd_x, uint16_t* wr_x, const QRegs (&Wc)[2],
                                            QRegs (&Wn)[2], const StageSrc& src1, const StageSrc& src2,
                                            const DqRow& T, StageSrc& src3, DqRow& T_n, Ops& carry, Ops& other,
@@ -297,7 +298,7 @@ __device__ __forceinline__ void stage_body(const LinearDev& L, const PrefillCtx&
         __builtin_amdgcn_sched_barrier(0);
     });
     // Last, so that no wait inside the regions has a scalar load to cover.
-    src3 = stage_src(L, st + 3, S);
+    src3 = stage_src(L, st + 3, lo, hi);
     T_n = kDq[src1.b];
 }
 
@@ -321,12 +322,22 @@ __device__ __forceinline__ float silu_mul_h(uint16_t g16, float u) {
     return g / (1.0f + expf(-g)) * u;
 }
 
-// One 256 x 256 output tile (rows m0.., columns n0..) over all of K.  GATED:
-// y already holds the gate product g (fp16) of the same tile, and the tile
-// stores SiLU(g) * acc over it.
+// A tile of a prefill plan cut along K into nparts pieces (part in K order):
+// each piece stores its fp32 sums to the plan's workspace and counts itself;
+// the last to arrive adds all pieces in K order and stores y.
+struct TilePart {
+    int part, nparts;
+    float* ws;               // nparts x [256 accumulators][256 threads] floats of this tile
+    uint32_t* counter;       // arrivals of this tile (zero between launches)
+};
+
+// One 256 x 256 output tile (rows m0.., columns n0..) over K-stages [lo, hi)
+// (a stage is half a group).  GATED: y already holds the gate product g
+// (fp16) of the same tile, and the tile stores SiLU(g) * acc over it.
 template <bool GATED>
-__device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, int n0, uint16_t* sxa,
-                                             uint16_t* sxb, uint16_t* sxc, uint16_t* sxd) {
+__device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, int n0, int lo, int hi,
+                                             const TilePart& tp, uint16_t* sxa, uint16_t* sxb, uint16_t* sxc,
+                                             uint16_t* sxd) {
     PrefillCtx c;
     c.tid = threadIdx.x;
     c.lane = c.tid & 63;
@@ -350,7 +361,6 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
         }
     }
 
-    const int S = 2 * L.G;
     f16v acc[2][8];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -364,13 +374,13 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
     DqRow T0;
     // The loop runs 4 stages per trip, each with its own x buffer; a stage
     // count of 2 mod 4 starts two stages early on zero x tiles and zero scales.
-    const int st0 = (S & 2) ? -2 : 0;
+    const int st0 = ((hi - lo) & 2) ? lo - 2 : lo;
     {
-        const StageSrc s0 = stage_src(L, st0, S);
-        s1 = stage_src(L, st0 + 1, S);
-        s2 = stage_src(L, st0 + 2, S);
+        const StageSrc s0 = stage_src(L, st0, lo, hi);
+        s1 = stage_src(L, st0 + 1, lo, hi);
+        s2 = stage_src(L, st0 + 2, lo, hi);
         T0 = kDq[s0.b];
-        if (st0 == 0) {
+        if (st0 == lo) {
 #pragma unroll
             for (int it = 0; it < 8; ++it) copy_x(c, s0, sxa, it);
 #pragma unroll
@@ -393,16 +403,16 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
     carry.a[0] = h8{};
     carry.a[1] = h8{};
     __syncthreads();
-    for (int st = st0; st < S; st += 4) {
+    for (int st = st0; st < hi; st += 4) {
         StageSrc s3, s4, s5, s6;
         DqRow T1, T2, T3, T4;
-        stage_body<true>(L, c, st, S, sxa, sxc, W0, W1, s1, s2, T0, s3, T1, carry, other, acc);
+        stage_body<true>(L, c, st, lo, hi, sxa, sxc, W0, W1, s1, s2, T0, s3, T1, carry, other, acc);
         stage_end();
-        stage_body<false>(L, c, st + 1, S, sxb, sxd, W1, W0, s2, s3, T1, s4, T2, carry, other, acc);
+        stage_body<false>(L, c, st + 1, lo, hi, sxb, sxd, W1, W0, s2, s3, T1, s4, T2, carry, other, acc);
         stage_end();
-        stage_body<true>(L, c, st + 2, S, sxc, sxa, W0, W1, s3, s4, T2, s5, T3, carry, other, acc);
+        stage_body<true>(L, c, st + 2, lo, hi, sxc, sxa, W0, W1, s3, s4, T2, s5, T3, carry, other, acc);
         stage_end();
-        stage_body<false>(L, c, st + 3, S, sxd, sxb, W1, W0, s4, s5, T3, s6, T4, carry, other, acc);
+        stage_body<false>(L, c, st + 3, lo, hi, sxd, sxb, W1, W0, s4, s5, T3, s6, T4, carry, other, acc);
         stage_end();
         s1 = s5;
         s2 = s6;
@@ -412,6 +422,61 @@ __device__ __forceinline__ void prefill_tile(const LinearDev& L, int M, int m0, 
     // The last stages' copies (of clamped stages, never read) land before
     // the tile ends, so none can reach the LDS of the next workgroup.
     __builtin_amdgcn_s_waitcnt((0 & 15) | ((0 >> 4) << 14) | (7 << 4) | (15 << 8));   // vmcnt(0)
+
+    if constexpr (!GATED) {
+        if (tp.nparts > 1) {
+            // Piece of a tile cut along K.  Accumulator k (= 16 (8 ib + jb) + e)
+            // of thread t goes to ws[part][k][t]: agent-scope stores, each
+            // thread waiting for its own before the barrier (a workgroup
+            // barrier does not wait for global stores), then one release count.
+            __shared__ uint32_t last;
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        __hip_atomic_store(tp.ws + ((size_t)tp.part * 256 + (16 * (8 * ib + jb) + e)) * kPThreads + c.tid,
+                                           acc[ib][jb][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt((0 & 15) | ((0 >> 4) << 14) | (7 << 4) | (15 << 8));   // vmcnt(0)
+            __syncthreads();
+            if (c.tid == 0)
+                last = __hip_atomic_fetch_add(tp.counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) ==
+                       (uint32_t)(tp.nparts - 1);
+            __syncthreads();
+            if (!last) return;
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            // The last piece adds the stored pieces (its own among them) in K
+            // order, whatever the arrival order, four outputs at a time.
+            const int lr = c.lane & 31, lh = c.lane >> 5;
+            for (int jb = 0; jb < 8; ++jb) {
+                const int m = m0 + 32 * jb + lr;
+                if (m >= M) continue;
+                for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const int n = n0 + 64 * c.wave + 32 * ib + 8 * a + 4 * lh;
+                        if (n >= L.N) continue;
+                        float o[4];
+                        for (int p = 0; p < tp.nparts; ++p) {
+                            const float* src = tp.ws + ((size_t)p * 256 + 16 * (8 * ib + jb) + 4 * a) * kPThreads + c.tid;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float v = __hip_atomic_load(src + e * kPThreads, __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_AGENT);
+                                o[e] = p == 0 ? v : o[e] + v;
+                            }
+                        }
+                        const uint32_t lo16 = (uint32_t)f32_to_f16_bits(o[0]) | ((uint32_t)f32_to_f16_bits(o[1]) << 16);
+                        const uint32_t hi16 = (uint32_t)f32_to_f16_bits(o[2]) | ((uint32_t)f32_to_f16_bits(o[3]) << 16);
+                        const u2v v = {lo16, hi16};
+                        *gptr_w<u2v>(L.y + (size_t)m * L.N + n) = v;
+                    }
+            }
+            if (c.tid == 0) __hip_atomic_store(tp.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+    }
 
     // Epilogue: lane holds rows m = 32 jb + lane % 32 and, per a, four
     // consecutive columns n = 64 wave + 32 ib + 8 a + 4 (lane / 32) + [0, 4).
@@ -454,14 +519,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(LinearDev L, int M, 
     const int j = (int)(blockIdx.x >> 3);
     const XcdBlock b = xcd_block(row_tiles, col_tiles, (int)(blockIdx.x & 7));
     if (j >= b.nr * b.nc) return;
-    prefill_tile<GATED>(L, M, (b.r0 + j % b.nr) * kPT, (b.c0 + j / b.nr) * kPT, sxa, sxb, sxc, sxd);
+    const TilePart whole{0, 1, nullptr, nullptr};
+    prefill_tile<GATED>(L, M, (b.r0 + j % b.nr) * kPT, (b.c0 + j / b.nr) * kPT, 0, 2 * L.G, whole, sxa, sxb, sxc,
+                        sxd);
 }
 
 // Several linears in one launch: workgroup i takes entry i of wg_map
 // (linear | tile << 16, tiles numbered row-major, or all ones: no tile); the
-// host orders the map longest-K first and XCD-aware.
+// host orders the map longest-K first and XCD-aware.  part_map[i] is
+// part | nparts << 4 | slot << 8: the tile's K-stages are cut into nparts
+// pieces of whole groups, this workgroup takes piece `part`, and a cut tile
+// uses workspace block `slot` (kPlanParts x 256 x 256 floats) and counter `slot`.
 __global__ __launch_bounds__(kPThreads) void prefill_plan_kernel(const LinearDev* __restrict__ list,
-                                                                  const uint32_t* __restrict__ wg_map, int M) {
+                                                                  const uint32_t* __restrict__ wg_map,
+                                                                  const uint32_t* __restrict__ part_map,
+                                                                  float* __restrict__ ws,
+                                                                  uint32_t* __restrict__ counters, int M) {
     __shared__ __attribute__((aligned(1024))) uint16_t sxa[kPXBytes / 2];
     __shared__ __attribute__((aligned(1024))) uint16_t sxb[kPXBytes / 2];
     __shared__ __attribute__((aligned(1024))) uint16_t sxc[kPXBytes / 2];
@@ -478,7 +551,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_plan_kernel(const LinearDev
             dst[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)src[k]);   // uniform: SGPRs
     }
     const int col_tiles = (L.N + kPT - 1) / kPT, t = (int)(e >> 16);
-    prefill_tile<false>(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, sxa, sxb, sxc, sxd);
+    const uint32_t pm = gptr<uint32_t>(part_map)[blockIdx.x];
+    const int part = (int)(pm & 15u), nparts = (int)((pm >> 4) & 15u);
+    const uint32_t slot = pm >> 8;
+    // Piece `part` of nparts: groups [G part / nparts, G (part + 1) / nparts).
+    const int lo = 2 * (L.G * part / nparts), hi = 2 * (L.G * (part + 1) / nparts);
+    const TilePart tp{part, nparts, ws + (size_t)slot * kPlanParts * 256 * kPThreads, counters + slot};
+    prefill_tile<false>(L, M, (t / col_tiles) * kPT, (t % col_tiles) * kPT, lo, hi, tp, sxa, sxb, sxc, sxd);
 }
 
 }  // namespace
@@ -529,9 +608,10 @@ int exq_prefill_tiles(const exq_layer* L, int M) {
     return t < 65536 ? (int)t : 0;
 }
 
-exq_status exq_prefill_plan_launch(const LinearDev* d_list, const uint32_t* d_wg_map, int total_wgs, int M,
-                                   hipStream_t stream) {
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3((unsigned)total_wgs), dim3(kPThreads), 0, stream, d_list, d_wg_map, M);
+exq_status exq_prefill_plan_launch(const LinearDev* d_list, const uint32_t* d_wg_map, const uint32_t* d_part_map,
+                                   float* d_ws, uint32_t* d_counters, int total_wgs, int M, hipStream_t stream) {
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3((unsigned)total_wgs), dim3(kPThreads), 0, stream, d_list, d_wg_map,
+                       d_part_map, d_ws, d_counters, M);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? EXQ_OK : fail(EXQ_ERR_HIP, "prefill plan launch: %s", hipGetErrorString(e));
 }

@@ -1,8 +1,10 @@
 """The five synthetic workloads at full size on the GPU, against the oracle.
 
 Packed bytes, scales and W_hat are compared bit for bit (W_hat for every
-linear of configs 1-4); outputs are compared on seeded samples of columns
-(and, at M = 2048, of rows) that the oracle computes one by one.
+linear of configs 1-4).  Outputs are compared on every column for configs 1,
+2 and 3 (every M), on every column of 64 seeded rows (plus the first and
+last) for config 4, and on seeded column samples for the 560 linears of
+config 5, the oracle computing each from packed storage or from W itself.
 """
 import numpy as np
 import pytest
@@ -62,19 +64,19 @@ def test_cfg1_uniform_4bit_4096(exq):
 
 def test_cfg2_mixed_8192(exq):
     spec = workloads.linears(2)[0]
-    check_linear(exq, spec, workloads.M_VALUES[2], ncols=512)
+    check_linear(exq, spec, workloads.M_VALUES[2], ncols=spec.N)
 
 
 @pytest.mark.parametrize("idx", range(7))
 def test_cfg3_block_linear(exq, idx):
     spec = workloads.linears(3)[idx]
-    check_linear(exq, spec, workloads.M_VALUES[3], ncols=256)
+    check_linear(exq, spec, workloads.M_VALUES[3], ncols=spec.N)
 
 
 @pytest.mark.parametrize("idx", range(7))
 def test_cfg4_prefill_linear(exq, idx):
     spec = workloads.linears(4)[idx]
-    check_linear(exq, spec, workloads.M_VALUES[4], ncols=96, nrows=32)
+    check_linear(exq, spec, workloads.M_VALUES[4], ncols=spec.N, nrows=64)
 
 
 CFG5_SAMPLE = (0, 6, 37 * 7 + 4, 79 * 7 + 1)
@@ -104,7 +106,7 @@ def test_cfg5_every_linear(exq):
         widths = workloads.make_widths(spec, W)
         q, s = exq.exq_pack(W, widths)
         layer = exq.Layer(spec.K, spec.N, widths, q, s)
-        cols = sample_cols(spec.N, 24, spec.w_seed() & 0xFFFF)
+        cols = sample_cols(spec.N, 64, spec.w_seed() & 0xFFFF)
         codes_c, scales_c = oracle.quantize(W[cols], widths)
         w_ref = oracle.dequant(codes_c, scales_c, widths)
         for M in (1, 16):
@@ -119,16 +121,17 @@ def test_cfg5_every_linear(exq):
 @pytest.mark.parametrize("M", [1, 16])
 def test_cfg3_block_as_one_plan(exq, M):
     """The seven linears of a 70B-shaped block as one decode plan (the launch
-    bench.py times), each checked on a column sample against the oracle."""
+    bench.py times), every output checked against the oracle (its own packed
+    layer, bit-exact with the library's)."""
     specs = workloads.linears(3)
     layers, refs, xs_h = [], [], []
     for spec in specs:
         W = workloads.make_weight(spec)
         widths = workloads.make_widths(spec, W)
         q, s = exq.exq_pack(W, widths)
-        cols = sample_cols(spec.N, 48, spec.w_seed() & 0xFFFF)
-        codes_c, scales_c = oracle.quantize(W[cols], widths)
-        refs.append((cols, oracle.dequant(codes_c, scales_c, widths)))
+        _, s_ref, q_ref = oracle.reference_layer(W, widths)
+        np.testing.assert_array_equal(q, q_ref)
+        refs.append((q_ref, s_ref, widths))
         layers.append(exq.Layer(spec.K, spec.N, widths, q, s))
         xs_h.append(workloads.make_x(spec, M))
         del W
@@ -137,9 +140,10 @@ def test_cfg3_block_as_one_plan(exq, M):
     note("cfg3 block plan M=%d" % M)
     plan = exq.Plan(layers, xs, ys, M)
     plan.run()
-    for spec, x, y, (cols, w_ref) in zip(specs, xs_h, ys, refs):
-        y_ref, bnd = oracle.gemm(x, w_ref)
-        assert_within(y_to_np(y)[:, cols], y_ref, bnd, "cfg3 plan %s M=%d" % (spec.name, M))
+    for spec, x, y, (q, s, widths) in zip(specs, xs_h, ys, refs):
+        cols = np.arange(spec.N, dtype=np.int64)
+        y_ref, bnd = oracle.gemm_packed_cols(x, q, s, widths, spec.K, spec.N, cols)
+        assert_within(y_to_np(y), y_ref, bnd, "cfg3 plan %s M=%d" % (spec.name, M))
     plan.close()
     for l in layers:
         l.close()
@@ -147,8 +151,9 @@ def test_cfg3_block_as_one_plan(exq, M):
 
 def test_cfg4_block_as_one_plan(exq):
     """The seven linears of a 70B-shaped block at M = 2048 as one prefill plan
-    (the launch bench.py times), each on a row and column sample against the
-    oracle, and the same bits on a second and third run."""
+    (the launch bench.py times, with the tiles of each XCD's last round cut
+    along K), every column of a row sample against the oracle, and the same
+    bits on a second and third run."""
     specs = workloads.linears(4)
     M = workloads.M_VALUES[4][0]
     rng = np.random.default_rng(M)
@@ -164,7 +169,7 @@ def test_cfg4_block_as_one_plan(exq):
         np.testing.assert_array_equal(q, q_ref)
         del W, codes
         layers.append(exq.Layer(spec.K, spec.N, widths, q, s))
-        refs.append((q_ref, s_ref, widths, sample_cols(spec.N, 48, spec.w_seed() & 0xFFFF)))
+        refs.append((q_ref, s_ref, widths, np.arange(spec.N, dtype=np.int64)))
         xs_h.append(workloads.make_x(spec, M))
     xs = [to_dev(x) for x in xs_h]
     ys = [torch.empty((M, l.N), dtype=torch.float16, device="cuda") for l in layers]

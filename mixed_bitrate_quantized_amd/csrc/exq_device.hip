@@ -171,10 +171,12 @@ __device__ __forceinline__ void group_compute(const DecodeCtx& c, const uint32_t
 template <int MB, int TC> struct Rows {
     static constexpr bool MMA = TC == 64 && MB >= 2;
     static constexpr int YB = MMA ? 4 : MB;
-    // Waves per SIMD the launch bounds ask for: the 16-row layout keeps two
-    // groups in flight per wave and fits 128 VGPRs, so two 8-wave workgroups
-    // share a CU (measured 1.2x faster than one with deeper pipelines).
-    static constexpr int WAVES_PER_EU = MMA ? 4 : 1;
+    // Waves per SIMD the launch bounds ask for: 4 (at most 128 VGPRs, two
+    // 8-wave workgroups per CU) for the 16-row layout, whose two groups in
+    // flight fit (measured 1.2x faster than one workgroup with deeper
+    // pipelines), and for M <= 4, whose pipelines fit too; the 16-column
+    // layout with more rows keeps its registers.
+    static constexpr int WAVES_PER_EU = (MMA || MB == 1) ? 4 : 1;
 };
 
 // The 16-row layout (64-column tiles, M > 4).  Lane (j = l / 16, c = l % 16)
@@ -224,6 +226,22 @@ __device__ __forceinline__ void group_compute_mma(const DecodeCtx& c, const uint
             float tv = acc[cb][0][i] * class_factor<B>(0);
             if constexpr (NCLS == 2) tv = __builtin_fmaf(acc[cb][1][i], class_factor<B>(2), tv);
             yacc[cb][i] = __builtin_fmaf(s, tv, yacc[cb][i]);
+        }
+    }
+}
+
+// Steps K, K+1, .. of a run's last partial round while K < rem, nested so
+// that each step is reached only from the one before it.  Guarded steps in
+// sequence (or a round that may end early and then reach the loop's back
+// edge) give the compiler's wait-count analysis paths, which the counts rule
+// out, on which loads are still in flight at the top of the next round; it
+// then drains every load there, every round.
+template <int K, int N, class F>
+__device__ __forceinline__ void tail_steps(int rem, F&& f) {
+    if constexpr (K < N) {
+        if (K < rem) {
+            f(IC<K>{});
+            tail_steps<K + 1, N>(rem, f);
         }
     }
 }
@@ -285,20 +303,49 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
         constexpr int k = decltype(KC)::value;
         issue(k, Q[k], S[k], X[k]);
     });
-    for (int i = 0; i < cnt; i += DEPTH) {
-        bool done = false;
+    auto compute = [&](auto KC) {
+        constexpr int k = decltype(KC)::value;
+        if constexpr (MMA) group_compute_mma<B, QS>(c, Q[k], X[k], S[k], yacc);
+        else group_compute<B, MB, TC, M1, QS>(c, Q[k], X[k], S[k][0], yacc);
+    };
+    if constexpr (MMA && B >= 5) {
+        // The 16-row layout's wide groups (4b code dwords per group in
+        // flight): guarded steps, and a round that ends the run leaves the
+        // loop at once.  The structure below spills here; this one does not,
+        // at the price of conservative waits inside a round.
+        for (int i = 0; i < cnt; i += DEPTH) {
+            bool done = false;
+            static_for<0, DEPTH>([&](auto KC) {
+                constexpr int k = decltype(KC)::value;
+                constexpr int nk = (k + DEPTH - 1) % DEPTH;
+                if (done || i + k >= cnt) {
+                    done = true;
+                    return;
+                }
+                issue(i + k + DEPTH - 1, Q[nk], S[nk], X[nk]);
+                compute(KC);
+            });
+            if (done) break;
+        }
+        return;
+    }
+    // Whole rounds of DEPTH steps with no exit inside, then the last partial
+    // round (see tail_steps).  Scheduling barriers close each step (and, for
+    // M <= 4, keep its loads ahead of its compute), so a step's loads stay
+    // in their step.
+    int i = 0;
+    for (; i + DEPTH <= cnt; i += DEPTH) {
         static_for<0, DEPTH>([&](auto KC) {
             constexpr int k = decltype(KC)::value;
             constexpr int nk = (k + DEPTH - 1) % DEPTH;
-            if (done || i + k >= cnt) {
-                done = true;
-                return;
-            }
             issue(i + k + DEPTH - 1, Q[nk], S[nk], X[nk]);
-            if constexpr (MMA) group_compute_mma<B, QS>(c, Q[k], X[k], S[k], yacc);
-            else group_compute<B, MB, TC, M1, QS>(c, Q[k], X[k], S[k][0], yacc);
+            if constexpr (!MMA) __builtin_amdgcn_sched_barrier(0);
+            compute(KC);
+            __builtin_amdgcn_sched_barrier(0);
         });
     }
+    // The last cnt - i < DEPTH groups are in flight already.
+    tail_steps<0, DEPTH - 1>(cnt - i, compute);
 }
 
 // One decode tile: TC columns, all of K, kWaves waves.  No prologue: every

@@ -251,16 +251,108 @@ template <int B, int TC> struct Depth {
     static constexpr int value = TC == 64 ? ((B <= 2) ? 4 : (B <= 4 ? 3 : 2)) : ((B <= 3) ? 6 : (B <= 6 ? 4 : 3));
 };
 
+// Activation ring of the 16-row layout in decode and plan launches: two
+// 4 KiB slots per wave, each one group's 16 rows x 128 activations.
+constexpr int kXSlot = 4096;
+constexpr int kXRing = 2 * kXSlot;
+
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// The 16-row layout's run with its activations staged in LDS.  Held in
+// registers, a group's activations are 4 loads of 16 bytes per lane in the
+// MFMA's operand order: each touches 32 cache lines for 1 KiB (row r's 16
+// bytes at 64-byte strides), and the vector memory pipeline stalls on the L1
+// cache.  Here 4 buffer loads with the LDS flag copy whole rows instead
+// (8 cache lines per KiB): copy i, lane l moves row r = 4i + l/16 (rows past
+// M repeat row M-1) and chunk (l % 16) ^ r of the group's 256 bytes to byte
+// 16 l of the slot's KiB i, so chunk ch of row r sits at 256 r + 16 (ch ^ r)
+// and the operand reads of 16 rows hit distinct banks.  Two groups in
+// flight, as in registers: step s issues group s+1 (ring slot (s+1) mod 2)
+// and waits until only those loads are in flight before reading group s.
+// The copies write LDS behind the compiler's back, hence the explicit count
+// and the scheduling barriers.
+template <int B, bool QS>
+__device__ __forceinline__ void run_width_mma_ring(const LinearDev& L, const DecodeCtx& c, const uint32_t* ord,
+                                                   int cnt, float (&yacc)[4][4], char* ring) {
+    using T = Width<B>;
+    constexpr int STEP = 4 * ((T::p0 == 8 ? 2 : 1) + (T::p1 > 0 ? 1 : 0) + 1) + 4;   // loads a step issues
+    static_assert(STEP < 64, "vmcnt range");
+    uint32_t Q[2][4 * B];
+    uint32_t S[2][4];   // fp16 scales (or scale-code bytes) in the low bits
+    // Read-only for the kernel: a constant-space load stays scalar although
+    // the copies count as memory writes.
+    const __attribute__((address_space(4))) uint32_t* og = (const __attribute__((address_space(4))) uint32_t*)ord;
+    const uint32_t N16 = 16u * (uint32_t)L.N;
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(L.x, 2u * (uint32_t)c.M * (uint32_t)L.K);
+    uint32_t xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + (c.lane >> 4);
+        xv[i] = 2u * (uint32_t)min(r, c.M - 1) * (uint32_t)L.K + 16u * (uint32_t)((c.lane & 15) ^ r);
+    }
+    auto issue = [&](int step, uint32_t (&Qd)[4 * B], uint32_t (&Sd)[4], int slot) {
+        const bool valid = step < cnt;
+        const uint32_t e = og[min(step, cnt - 1)];
+        const uint32_t g = e & 0xFFFFu, P = e >> 16;
+        char* dst = ring + slot * kXSlot;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(dst + 1024 * i), 16, (int)xv[i], (int)(256u * g),
+                                                     0, 0);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const uint32_t n = (uint32_t)(c.n + 16 * cb);
+            const uint32_t col = valid ? 16u * ((uint32_t)L.N * P + n) : kBufOOB;
+            load_quarter<B>(c.rw, col, N16, c.q, *reinterpret_cast<uint32_t(*)[B]>(Qd + cb * B));
+            if constexpr (QS) {
+                const uint32_t soff = valid ? g * ((uint32_t)L.N >> 1) + (n >> 1) : kBufOOB;
+                Sd[cb] = __builtin_amdgcn_raw_buffer_load_b8(c.rs, soff, 0, 0);
+            } else {
+                const uint32_t soff = valid ? 2u * (g * (uint32_t)L.N + n) : kBufOOB;
+                Sd[cb] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, soff, 0, 0);
+            }
+        }
+    };
+    // Group in slot k once at most `wait` loads are in flight.
+    auto compute = [&](auto KC, auto WC) {
+        constexpr int k = decltype(KC)::value;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(WC)::value));
+        __builtin_amdgcn_sched_barrier(0);
+        const int r = c.lane & 15;
+        const char* src = ring + k * kXSlot + 256 * r;
+        u4v X[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) X[kk] = *reinterpret_cast<const u4v*>(src + 16 * ((4 * c.q + kk) ^ r));
+        const uint16_t s16[4] = {(uint16_t)S[k][0], (uint16_t)S[k][1], (uint16_t)S[k][2], (uint16_t)S[k][3]};
+        group_compute_mma<B, QS>(c, Q[k], X, s16, yacc);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    issue(0, Q[0], S[0], 0);
+    int i = 0;
+    for (; i + 2 <= cnt; i += 2) {
+        static_for<0, 2>([&](auto KC) {
+            constexpr int k = decltype(KC)::value;
+            issue(i + k + 1, Q[(k + 1) % 2], S[(k + 1) % 2], (k + 1) % 2);
+            compute(KC, IC<STEP>{});
+        });
+    }
+    if (i < cnt) compute(IC<0>{}, IC<0>{});   // nothing was issued after the last group
+}
+
 // A run of `cnt` width-B groups (entries ord[0..cnt)), pipelined DEPTH deep:
 // while group i is computed, groups i+1 .. i+DEPTH-1 are in flight.  Every
 // step issues exactly one group's loads -- weights, scale, activation
 // operands, in that order -- so each wait is a compile-time count.  Steps
 // past the end of the run load from an out-of-range buffer offset: they
 // keep the count fixed, return zeros and cost no memory traffic.
-template <int B, int MB, int TC, bool M1, bool QS>
+template <int B, int MB, int TC, bool M1, bool QS, bool XR>
 __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c, const uint32_t* ord, int cnt,
-                                          float (&yacc)[Rows<MB, TC>::YB][4]) {
+                                          float (&yacc)[Rows<MB, TC>::YB][4], char* ring) {
     constexpr bool MMA = Rows<MB, TC>::MMA;
+    if constexpr (MMA && XR && B <= 4) {
+        run_width_mma_ring<B, QS>(L, c, ord, cnt, yacc, ring);
+        return;
+    }
     constexpr int DEPTH = MMA ? 2 : Depth<B, TC>::value;
     constexpr int NDW = MMA ? 4 * B : B * Tile<TC>::NQ;
     constexpr int NS = MMA ? 4 : 1;             // scales per lane and group
@@ -352,10 +444,14 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
 // wave starts streaming at once and only the final reduction is shared.
 // decode_stream leaves each wave's partial sums in red (kWaves x M x TC
 // fp32); after a workgroup barrier the waves are added in order.
-template <int MB, int TC, bool M1, bool QS>
-__device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int M, float* red) {
+// XR (16-row layout only): activations go through per-wave rings at xlds,
+// memory that red reuses once every wave has finished its runs.
+template <int MB, int TC, bool M1, bool QS, bool XR = false>
+__device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int M, float* red, char* xlds = nullptr) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    static_assert(!XR || Rows<MB, TC>::MMA, "activation rings belong to the 16-row layout");
+    char* ring = XR ? xlds + wave * kXRing : nullptr;
     constexpr bool MMA = Rows<MB, TC>::MMA;
     constexpr int YB = Rows<MB, TC>::YB;
     DecodeCtx c;
@@ -389,16 +485,22 @@ __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int 
         const uint32_t* ord = L.order + gptr<uint16_t>(L.bounds)[wave];
         const EXQ_GLOBAL uint16_t* cnt = gptr<uint16_t>(L.runs) + wave * kNumWidths;
         int k;
-        if ((k = cnt[0]) > 0) { run_width<2, MB, TC, M1, QS>(L, c, ord, k, yacc); ord += k; }
-        if ((k = cnt[1]) > 0) { run_width<3, MB, TC, M1, QS>(L, c, ord, k, yacc); ord += k; }
-        if ((k = cnt[2]) > 0) { run_width<4, MB, TC, M1, QS>(L, c, ord, k, yacc); ord += k; }
-        if ((k = cnt[3]) > 0) { run_width<5, MB, TC, M1, QS>(L, c, ord, k, yacc); ord += k; }
-        if ((k = cnt[4]) > 0) { run_width<6, MB, TC, M1, QS>(L, c, ord, k, yacc); ord += k; }
-        if ((k = cnt[5]) > 0) { run_width<8, MB, TC, M1, QS>(L, c, ord, k, yacc); }
+        if ((k = cnt[0]) > 0) { run_width<2, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); ord += k; }
+        if ((k = cnt[1]) > 0) { run_width<3, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); ord += k; }
+        if ((k = cnt[2]) > 0) { run_width<4, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); ord += k; }
+        if ((k = cnt[3]) > 0) { run_width<5, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); ord += k; }
+        if ((k = cnt[4]) > 0) { run_width<6, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); ord += k; }
+        if ((k = cnt[5]) > 0) { run_width<8, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); }
     }
 
     // 16-row layout: every (row, column) of the tile belongs to one lane.
     if constexpr (MMA) {
+        if constexpr (XR) {
+            // Every copy into the rings has landed and every wave has left
+            // its runs before red overwrites them.
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __syncthreads();
+        }
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -432,9 +534,9 @@ __device__ __forceinline__ float tile_sum(const float* red, int M, int m, int co
     return v;
 }
 
-template <int MB, int TC, bool M1, bool QS>
-__device__ __forceinline__ void decode_wg(const LinearDev& L, int tile, int M, float* red) {
-    decode_stream<MB, TC, M1, QS>(L, tile, M, red);
+template <int MB, int TC, bool M1, bool QS, bool XR = false>
+__device__ __forceinline__ void decode_wg(const LinearDev& L, int tile, int M, float* red, char* xlds = nullptr) {
+    decode_stream<MB, TC, M1, QS, XR>(L, tile, M, red, xlds);
     __syncthreads();
     for (int t = threadIdx.x; t < M * TC; t += kWaves * 64) {
         const int m = t / TC, col = t % TC;
@@ -463,16 +565,23 @@ __global__ __launch_bounds__(kWaves * 64, (Rows<MB, TC>::WAVES_PER_EU)) void gat
     }
 }
 
+// LDS of a decode workgroup: the wave partials and, in the 16-row layout,
+// the activation rings, which the partials reuse.
+template <int MB, int TC> struct DecodeLds {
+    static constexpr int RED = kWaves * 4 * MB * TC * 4;
+    static constexpr int BYTES = Rows<MB, TC>::MMA && kWaves * kXRing > RED ? kWaves * kXRing : RED;
+};
+
 template <int MB, int TC, bool M1, bool QS>
 __global__ __launch_bounds__(kWaves * 64, (Rows<MB, TC>::WAVES_PER_EU)) void decode_kernel(LinearDev L, int M) {
-    __shared__ float red[kWaves * 4 * MB * TC];
-    decode_wg<MB, TC, M1, QS>(L, blockIdx.x, M, red);
+    __shared__ __attribute__((aligned(16))) char lds[DecodeLds<MB, TC>::BYTES];
+    decode_wg<MB, TC, M1, QS, Rows<MB, TC>::MMA>(L, blockIdx.x, M, reinterpret_cast<float*>(lds), lds);
 }
 
 template <int MB, bool M1, bool QS>
 __global__ __launch_bounds__(kWaves * 64, (Rows<MB, 64>::WAVES_PER_EU)) void decode_plan_kernel(const LinearDev* __restrict__ list,
                                                                    const uint32_t* __restrict__ wg_map, int M) {
-    __shared__ float red[kWaves * 4 * MB * 64];
+    __shared__ __attribute__((aligned(16))) char lds[DecodeLds<MB, 64>::BYTES];
     const uint32_t e = gptr<uint32_t>(wg_map)[blockIdx.x];   // linear | tile << 16
     LinearDev L;
     {
@@ -483,7 +592,7 @@ __global__ __launch_bounds__(kWaves * 64, (Rows<MB, 64>::WAVES_PER_EU)) void dec
         for (int i = 0; i < (int)(sizeof(LinearDev) / 4); ++i)
             dst[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)src[i]);   // uniform: SGPRs
     }
-    decode_wg<MB, 64, M1, QS>(L, (int)(e >> 16), M, red);
+    decode_wg<MB, 64, M1, QS, Rows<MB, 64>::MMA>(L, (int)(e >> 16), M, reinterpret_cast<float*>(lds), lds);
 }
 
 // ------------------------------------------------- quantized scale expansion

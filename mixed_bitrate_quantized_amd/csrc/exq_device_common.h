@@ -55,6 +55,9 @@ template <class T> __device__ __forceinline__ const EXQ_GLOBAL T* gptr(const voi
 }
 template <class T> __device__ __forceinline__ EXQ_GLOBAL T* gptr_w(void* p) { return (EXQ_GLOBAL T*)p; }
 
+// LDS destination of a buffer load that writes LDS directly.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 template <int I> using IC = std::integral_constant<int, I>;
 
 template <int B, int E, class F>

@@ -136,7 +136,6 @@ __device__ __forceinline__ void issue_w(const LinearDev& L, const PrefillCtx& c,
 // (i % 8) ^ xswz(row) of row 64 w + 8 it + i / 8.  The stage's position in K
 // goes in the scalar offset; rows past M fail the range check of the
 // vector offset and read zeros.
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ void copy_x(const PrefillCtx& c, const StageSrc& src, uint16_t* sx, int it) {
     const uint32_t soff = 256u * src.g + 128u * src.h;
     char* dst = reinterpret_cast<char*>(sx) + 1024 * (8 * c.wave + it);

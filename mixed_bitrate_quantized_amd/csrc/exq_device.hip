@@ -349,7 +349,9 @@ template <int B, int MB, int TC, bool M1, bool QS, bool XR>
 __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c, const uint32_t* ord, int cnt,
                                           float (&yacc)[Rows<MB, TC>::YB][4], char* ring) {
     constexpr bool MMA = Rows<MB, TC>::MMA;
-    if constexpr (MMA && XR && B <= 4) {
+    // Activation rings for widths up to 6 bits (4 with quantized scales,
+    // whose kernels spill otherwise); 8-bit groups keep the register path.
+    if constexpr (MMA && XR && B <= (QS ? 4 : 6)) {
         run_width_mma_ring<B, QS>(L, c, ord, cnt, yacc, ring);
         return;
     }

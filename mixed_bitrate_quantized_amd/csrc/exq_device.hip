@@ -218,14 +218,18 @@ __device__ __forceinline__ void group_compute_mma(const DecodeCtx& c, const uint
             acc[cb][cls] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, wop, acc[cb][cls], 0, 0, 0);
         }
     });
+    // Each class's factor goes into the scale (exact: a power of two times an
+    // fp16 value), so each row takes one product per class.
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const float s = group_scale<B, QS>(c.ref4[cb], c.n + 16 * cb, S[cb]);
+        const float s0 = s * class_factor<B>(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float tv = acc[cb][0][i] * class_factor<B>(0);
-            if constexpr (NCLS == 2) tv = __builtin_fmaf(acc[cb][1][i], class_factor<B>(2), tv);
-            yacc[cb][i] = __builtin_fmaf(s, tv, yacc[cb][i]);
+        for (int i = 0; i < 4; ++i) yacc[cb][i] = __builtin_fmaf(s0, acc[cb][0][i], yacc[cb][i]);
+        if constexpr (NCLS == 2) {
+            const float s2 = s * class_factor<B>(2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yacc[cb][i] = __builtin_fmaf(s2, acc[cb][1][i], yacc[cb][i]);
         }
     }
 }

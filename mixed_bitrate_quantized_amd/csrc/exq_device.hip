@@ -250,10 +250,20 @@ __device__ __forceinline__ void tail_steps(int rem, F&& f) {
     }
 }
 
-template <int B, int TC> struct Depth {
-    // groups in flight per wave (the one being computed included)
-    static constexpr int value = TC == 64 ? ((B <= 2) ? 4 : (B <= 4 ? 3 : 2)) : ((B <= 3) ? 6 : (B <= 6 ? 4 : 3));
+template <int B, int TC, bool WIDE = false> struct Depth {
+    // groups in flight per wave (the one being computed included); WIDE:
+    // the high-occupancy plan kernel (8 waves per SIMD, 64 VGPRs)
+    static constexpr int value = WIDE ? (B <= 4 ? 2 : 1)
+                               : TC == 64 ? ((B <= 2) ? 4 : (B <= 4 ? 3 : 2)) : ((B <= 3) ? 6 : (B <= 6 ? 4 : 3));
 };
+
+// Plans at M <= 4 with at least this many workgroups per compute unit run
+// the high-occupancy kernel: four 8-wave workgroups per CU with shallower
+// pipelines instead of two with deeper ones.  On the 70B block (1312
+// workgroups) it measured 5 % faster at M = 1 and M = 4; a single linear
+// (fewer workgroups than CUs) took twice as long with it, its waves' own
+// pipelines being all that hides the memory latency.
+constexpr int kWideWgsPerCu = 4;
 
 // Activation ring of the 16-row layout in decode and plan launches: two
 // 4 KiB slots per wave, each one group's 16 rows x 128 activations.
@@ -349,7 +359,7 @@ __device__ __forceinline__ void run_width_mma_ring(const LinearDev& L, const Dec
 // operands, in that order -- so each wait is a compile-time count.  Steps
 // past the end of the run load from an out-of-range buffer offset: they
 // keep the count fixed, return zeros and cost no memory traffic.
-template <int B, int MB, int TC, bool M1, bool QS, bool XR>
+template <int B, int MB, int TC, bool M1, bool QS, bool XR, bool WIDE = false>
 __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c, const uint32_t* ord, int cnt,
                                           float (&yacc)[Rows<MB, TC>::YB][4], char* ring) {
     constexpr bool MMA = Rows<MB, TC>::MMA;
@@ -359,7 +369,8 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
         run_width_mma_ring<B, QS>(L, c, ord, cnt, yacc, ring);
         return;
     }
-    constexpr int DEPTH = MMA ? 2 : Depth<B, TC>::value;
+    static_assert(!WIDE || (!MMA && TC == 64), "the high-occupancy kernel is the 64-column 4x4x4 layout");
+    constexpr int DEPTH = MMA ? 2 : Depth<B, TC, WIDE>::value;
     constexpr int NDW = MMA ? 4 * B : B * Tile<TC>::NQ;
     constexpr int NS = MMA ? 4 : 1;             // scales per lane and group
     constexpr int NX = MMA ? 4 : MB;            // activation operands per lane and group
@@ -452,7 +463,7 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
 // fp32); after a workgroup barrier the waves are added in order.
 // XR (16-row layout only): activations go through per-wave rings at xlds,
 // memory that red reuses once every wave has finished its runs.
-template <int MB, int TC, bool M1, bool QS, bool XR = false>
+template <int MB, int TC, bool M1, bool QS, bool XR = false, bool WIDE = false>
 __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int M, float* red, char* xlds = nullptr) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -491,12 +502,12 @@ __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int 
         const uint32_t* ord = L.order + gptr<uint16_t>(L.bounds)[wave];
         const EXQ_GLOBAL uint16_t* cnt = gptr<uint16_t>(L.runs) + wave * kNumWidths;
         int k;
-        if ((k = cnt[0]) > 0) { run_width<2, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); ord += k; }
-        if ((k = cnt[1]) > 0) { run_width<3, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); ord += k; }
-        if ((k = cnt[2]) > 0) { run_width<4, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); ord += k; }
-        if ((k = cnt[3]) > 0) { run_width<5, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); ord += k; }
-        if ((k = cnt[4]) > 0) { run_width<6, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); ord += k; }
-        if ((k = cnt[5]) > 0) { run_width<8, MB, TC, M1, QS, XR>(L, c, ord, k, yacc, ring); }
+        if ((k = cnt[0]) > 0) { run_width<2, MB, TC, M1, QS, XR, WIDE>(L, c, ord, k, yacc, ring); ord += k; }
+        if ((k = cnt[1]) > 0) { run_width<3, MB, TC, M1, QS, XR, WIDE>(L, c, ord, k, yacc, ring); ord += k; }
+        if ((k = cnt[2]) > 0) { run_width<4, MB, TC, M1, QS, XR, WIDE>(L, c, ord, k, yacc, ring); ord += k; }
+        if ((k = cnt[3]) > 0) { run_width<5, MB, TC, M1, QS, XR, WIDE>(L, c, ord, k, yacc, ring); ord += k; }
+        if ((k = cnt[4]) > 0) { run_width<6, MB, TC, M1, QS, XR, WIDE>(L, c, ord, k, yacc, ring); ord += k; }
+        if ((k = cnt[5]) > 0) { run_width<8, MB, TC, M1, QS, XR, WIDE>(L, c, ord, k, yacc, ring); }
     }
 
     // 16-row layout: every (row, column) of the tile belongs to one lane.
@@ -540,9 +551,9 @@ __device__ __forceinline__ float tile_sum(const float* red, int M, int m, int co
     return v;
 }
 
-template <int MB, int TC, bool M1, bool QS, bool XR = false>
+template <int MB, int TC, bool M1, bool QS, bool XR = false, bool WIDE = false>
 __device__ __forceinline__ void decode_wg(const LinearDev& L, int tile, int M, float* red, char* xlds = nullptr) {
-    decode_stream<MB, TC, M1, QS, XR>(L, tile, M, red, xlds);
+    decode_stream<MB, TC, M1, QS, XR, WIDE>(L, tile, M, red, xlds);
     __syncthreads();
     for (int t = threadIdx.x; t < M * TC; t += kWaves * 64) {
         const int m = t / TC, col = t % TC;
@@ -584,8 +595,8 @@ __global__ __launch_bounds__(kWaves * 64, (Rows<MB, TC>::WAVES_PER_EU)) void dec
     decode_wg<MB, TC, M1, QS, Rows<MB, TC>::MMA>(L, blockIdx.x, M, reinterpret_cast<float*>(lds), lds);
 }
 
-template <int MB, bool M1, bool QS>
-__global__ __launch_bounds__(kWaves * 64, (Rows<MB, 64>::WAVES_PER_EU)) void decode_plan_kernel(const LinearDev* __restrict__ list,
+template <int MB, bool M1, bool QS, bool WIDE>
+__global__ __launch_bounds__(kWaves * 64, (WIDE ? 8 : Rows<MB, 64>::WAVES_PER_EU)) void decode_plan_kernel(const LinearDev* __restrict__ list,
                                                                    const uint32_t* __restrict__ wg_map, int M) {
     __shared__ __attribute__((aligned(16))) char lds[DecodeLds<MB, 64>::BYTES];
     const uint32_t e = gptr<uint32_t>(wg_map)[blockIdx.x];   // linear | tile << 16
@@ -598,7 +609,7 @@ __global__ __launch_bounds__(kWaves * 64, (Rows<MB, 64>::WAVES_PER_EU)) void dec
         for (int i = 0; i < (int)(sizeof(LinearDev) / 4); ++i)
             dst[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)src[i]);   // uniform: SGPRs
     }
-    decode_wg<MB, 64, M1, QS, Rows<MB, 64>::MMA>(L, (int)(e >> 16), M, reinterpret_cast<float*>(lds), lds);
+    decode_wg<MB, 64, M1, QS, Rows<MB, 64>::MMA, WIDE>(L, (int)(e >> 16), M, reinterpret_cast<float*>(lds), lds);
 }
 
 // ------------------------------------------------- quantized scale expansion
@@ -729,6 +740,7 @@ struct exq_plan {
     int count = 0, M = 1, total_wgs = 0;
     bool prefill = false;   // M > 16: prefill tiles, else decode column tiles
     bool qs = false;        // decode plan of layers with quantized scales
+    bool wide = false;      // decode plan at M <= 4 run by the high-occupancy kernel
     LinearDev* d_list = nullptr;
     uint32_t* d_wg_map = nullptr;
     uint32_t* d_part_map = nullptr;   // prefill: K-piece of each workgroup's tile
@@ -838,14 +850,25 @@ exq_status launch_decode(const LinearDev& d, int M, hipStream_t stream) {
     return e == hipSuccess ? EXQ_OK : hip_fail(e, "decode launch");
 }
 
+template <int MB, bool M1, bool WIDE>
+void launch_plan_w(const exq_plan* P, hipStream_t s) {
+    if (P->qs)
+        hipLaunchKernelGGL((decode_plan_kernel<MB, M1, true, WIDE>), dim3(P->total_wgs), dim3(kWaves * 64), 0, s,
+                           P->d_list, P->d_wg_map, P->M);
+    else
+        hipLaunchKernelGGL((decode_plan_kernel<MB, M1, false, WIDE>), dim3(P->total_wgs), dim3(kWaves * 64), 0, s,
+                           P->d_list, P->d_wg_map, P->M);
+}
+
 template <int MB, bool M1>
 void launch_plan_t(const exq_plan* P, hipStream_t s) {
-    if (P->qs)
-        hipLaunchKernelGGL((decode_plan_kernel<MB, M1, true>), dim3(P->total_wgs), dim3(kWaves * 64), 0, s, P->d_list,
-                           P->d_wg_map, P->M);
-    else
-        hipLaunchKernelGGL((decode_plan_kernel<MB, M1, false>), dim3(P->total_wgs), dim3(kWaves * 64), 0, s, P->d_list,
-                           P->d_wg_map, P->M);
+    if constexpr (MB == 1) {
+        if (P->wide) {
+            launch_plan_w<1, M1, true>(P, s);
+            return;
+        }
+    }
+    launch_plan_w<MB, M1, false>(P, s);
 }
 
 void launch_plan(const exq_plan* P, hipStream_t s) {
@@ -1366,6 +1389,16 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
     P->qs = !prefill && layers[0]->qs;
     P->total_wgs = (int)wg_map.size();
     hipError_t e;
+    if (!prefill && M <= 4) {
+        int dev = 0, cus = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess ||
+            (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) {
+            exq_plan_destroy(P);
+            return hip_fail(e, "compute unit count");
+        }
+        // fp16 scales only: with quantized scales the kernel spills at 64 VGPRs.
+        P->wide = !P->qs && P->total_wgs >= kWideWgsPerCu * cus;
+    }
     if ((e = hipMalloc(&P->d_list, sizeof(LinearDev) * count)) != hipSuccess ||
         (e = hipMalloc(&P->d_wg_map, sizeof(uint32_t) * wg_map.size())) != hipSuccess) {
         exq_plan_destroy(P);

@@ -1,24 +1,26 @@
 // Device half of libexq for gfx950: decode GEMV, dequantization, layer and
 // plan management.  The prefill GEMM (M > 16) lives in exq_prefill.hip.
 //
-// Decode design (M <= 16, HBM-bound):
-//   * a workgroup owns 16 output columns over the whole of K; its 8 waves
-//     share the groups, pre-sorted by width and cut into instruction-balanced
-//     chunks, so a wave streams one or two runs of equal-width groups and its
-//     software pipeline waits on compile-time load counts;
-//   * lane l handles column l % 16 and K-quarter q = l / 16 of every group:
-//     it loads exactly the 4*b bytes of EXQ1 storage that hold codes
-//     [32q, 32q+32) of its column, and the 16 lanes of a quarter read
-//     contiguous 256-byte runs;
+// Decode design (M <= 16 per launch; larger M in 16-row slices):
+//   * a workgroup owns 64 output columns (16 when N % 64 != 0) over the whole
+//     of K; its 8 waves share the groups, pre-sorted by width and cut into
+//     instruction-balanced chunks, so a wave streams one or two runs of
+//     equal-width groups, each pipelined a fixed number of groups deep with
+//     compile-time load counts (whole rounds, then the last partial round);
 //   * a code field is masked in place into the low bits of an fp16 half,
 //     which then *is* the fp16 value c * 2^(o-24) (a subnormal): one AND per
 //     two weights, no conversion; one packed fp16 add of -z * 2^(o-24) then
 //     gives (c - z) * 2^(o-24) exactly (every operand and the result are
 //     multiples of 2^-24 below 2^-14), so a weight whose code is the zero
 //     point contributes an exact zero whatever its activation;
-//   * the multiply-accumulate runs on the matrix cores with
-//     v_mfma_f32_4x4x4_16b_f16; each 16-lane quarter is a set of four 4x4
-//     blocks that shares one activation block (cbsz = 2);
+//   * M <= 4: lane l owns column l of the tile over the whole group (or
+//     K-quarter l / 16 of column l % 16 in 16-column tiles), and
+//     v_mfma_f32_4x4x4_16b_f16 multiplies with one activation block shared
+//     by a set of 4x4 blocks (cbsz); a plan with at least 4 workgroups per
+//     CU runs a high-occupancy instance (64 VGPRs, shallower pipelines);
+//   * M = 5..16: the 16-row layout on v_mfma_f32_16x16x32_f16 (lane (j, c):
+//     K-quarter j of columns c, c+16, c+32, c+48), with each group's
+//     activations staged in a per-wave LDS ring for widths up to 6 bits;
 //   * per group the per-offset partial sums are rescaled by 2^(24-o) and
 //     the fp16 scale is applied in fp32:  y += s * sum x * (c - z);
 //   * quarters and waves are reduced in a fixed order: no atomics, the result

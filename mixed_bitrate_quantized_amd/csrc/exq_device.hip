@@ -1398,7 +1398,7 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
             exq_plan_destroy(P);
             return hip_fail(e, "compute unit count");
         }
-        // fp16 scales only: with quantized scales the kernel spills at 64 VGPRs.
+        // fp16 scales only: with quantized scales it measured slower than the deep kernel.
         P->wide = !P->qs && P->total_wgs >= kWideWgsPerCu * cus;
     }
     if ((e = hipMalloc(&P->d_list, sizeof(LinearDev) * count)) != hipSuccess ||

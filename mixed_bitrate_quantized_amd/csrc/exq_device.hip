@@ -9,10 +9,11 @@
 //     compile-time load counts (whole rounds, then the last partial round);
 //   * a code field is masked in place into the low bits of an fp16 half,
 //     which then *is* the fp16 value c * 2^(o-24) (a subnormal): one AND per
-//     two weights, no conversion; one packed fp16 add of -z * 2^(o-24) then
-//     gives (c - z) * 2^(o-24) exactly (every operand and the result are
-//     multiples of 2^-24 below 2^-14), so a weight whose code is the zero
-//     point contributes an exact zero whatever its activation;
+//     two weights, no conversion; one packed fp16 FMA by 2^-o with addend
+//     -z * 2^-24 then gives (c - z) * 2^-24 exactly (the product and the
+//     result are multiples of 2^-24 below 2^-14), so a weight whose code is
+//     the zero point contributes an exact zero whatever its activation, and
+//     fields at every bit offset feed one accumulator;
 //   * M <= 4: lane l owns column l of the tile over the whole group (or
 //     K-quarter l / 16 of column l % 16 in 16-column tiles), and
 //     v_mfma_f32_4x4x4_16b_f16 multiplies with one activation block shared
@@ -21,8 +22,8 @@
 //   * M = 5..16: the 16-row layout on v_mfma_f32_16x16x32_f16 (lane (j, c):
 //     K-quarter j of columns c, c+16, c+32, c+48), with each group's
 //     activations staged in a per-wave LDS ring for widths up to 6 bits;
-//   * per group the per-offset partial sums are rescaled by 2^(24-o) and
-//     the fp16 scale is applied in fp32:  y += s * sum x * (c - z);
+//   * per group the partial sum is rescaled by 2^24 and the fp16 scale is
+//     applied in fp32:  y += s * sum x * (c - z);
 //   * quarters and waves are reduced in a fixed order: no atomics, the result
 //     is deterministic.
 #include <hip/hip_runtime.h>
@@ -40,36 +41,70 @@ namespace exq {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
-template <int B> __device__ constexpr float class_factor(int t) {
-    // 2^(24 - o), o = p0 * t: turns c * 2^(o-24) back into c.
-    return (float)(1u << (24 - Width<B>::p0 * t));
+// 2^24: the decoded weights are (c - z) * 2^-24 (see unbias); a wave's
+// partial sums are multiplied by it once, on their way out.  With fp32
+// partials far above the subnormal range (|x|, s >= 2^-24 give products of
+// at least 2^-72) the power of two commutes exactly with every product and
+// sum, so the result is bit for bit the one of unscaled arithmetic.
+constexpr float kUnit = 16777216.0f;
+
+// P_DW consecutive dwords at byte voff + soff of a buffer (voff per lane,
+// soff uniform); aux 2: streamed once.
+template <int P_DW>
+__device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t rw, uint32_t voff, uint32_t soff, uint32_t* dst) {
+    if constexpr (P_DW == 1) {
+        dst[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff, soff, 2);
+    } else if constexpr (P_DW == 2) {
+        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rw, voff, soff, 2);
+        dst[0] = v[0];
+        dst[1] = v[1];
+    } else {
+        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, voff, soff, 2);
+        dst[0] = v[0];
+        dst[1] = v[1];
+        dst[2] = v[2];
+        dst[3] = v[3];
+    }
 }
 
+// Where quarter q of a column's group words sits.  Column-local dword m of a
+// group is dword m % 4 of word m / 4, and word j of column n lies at byte
+// 16 (N (P + j) + n) of the weight buffer (P: the group's first word row).
+// Plane 0 of quarter q is dwords [p0 q, p0 (q + 1)), plane 1 (if any)
+// [4 p0 + p1 q, 4 p0 + p1 (q + 1)).  v0 and v1 are the per-lane parts of
+// the two planes' byte offsets (column and quarter); the uniform rest,
+// 16 N P (plus 16 N p0 for plane 1), comes with the group.
+struct QuarterOffsets {
+    uint32_t v0, v1;
+};
 template <int B>
-__device__ __forceinline__ void load_quarter(__amdgpu_buffer_rsrc_t rw, uint32_t col, uint32_t N16, int q,
-                                             uint32_t (&Q)[B]) {
+__device__ __forceinline__ QuarterOffsets quarter_offsets(uint32_t n16, int q, uint32_t N16) {
+    using T = Width<B>;
+    const uint32_t m0 = (uint32_t)(T::p0 * q), m1 = (uint32_t)(T::p1 * q);
+    return {n16 + (m0 >> 2) * N16 + 4u * (m0 & 3u), n16 + (m1 >> 2) * N16 + 4u * (m1 & 3u)};
+}
+
+// The B dwords of one quarter: plane 0's then plane 1's.  soff = 16 N P.
+template <int B>
+__device__ __forceinline__ void load_quarter(__amdgpu_buffer_rsrc_t rw, const QuarterOffsets& o, uint32_t soff,
+                                             uint32_t N16, uint32_t (&Q)[B]) {
     using T = Width<B>;
     if constexpr (T::p0 == 8) {
-        load_piece<4>(rw, col, N16, 8 * q, Q);
-        load_piece<4>(rw, col, N16, 8 * q + 4, Q + 4);
+        load_dwords<4>(rw, o.v0, soff, Q);
+        load_dwords<4>(rw, o.v0, soff + N16, Q + 4);
     } else {
-        load_piece<T::p0>(rw, col, N16, T::p0 * q, Q);
+        load_dwords<T::p0>(rw, o.v0, soff, Q);
     }
-    if constexpr (T::p1 > 0) load_piece<T::p1>(rw, col, N16, 4 * T::p0 + T::p1 * q, Q + T::p0);
+    if constexpr (T::p1 > 0) load_dwords<T::p1>(rw, o.v1, soff + (uint32_t)T::p0 * N16, Q + T::p0);
 }
 
-// All B words of one column of a group (one 1 KB wave load each).
+// All B words of one column of a group (one 1 KB wave load each): per-lane
+// n16 = 16 n, uniform soff = 16 N P.
 template <int B>
-__device__ __forceinline__ void load_group_words(__amdgpu_buffer_rsrc_t rw, uint32_t col, uint32_t N16,
-                                                 uint32_t (&D)[4 * B]) {
+__device__ __forceinline__ void load_group_words(__amdgpu_buffer_rsrc_t rw, uint32_t n16, uint32_t soff,
+                                                 uint32_t N16, uint32_t (&D)[4 * B]) {
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, col + (uint32_t)j * N16, 0, 2);
-        D[4 * j + 0] = v[0];
-        D[4 * j + 1] = v[1];
-        D[4 * j + 2] = v[2];
-        D[4 * j + 3] = v[3];
-    }
+    for (int j = 0; j < B; ++j) load_dwords<4>(rw, n16, soff + (uint32_t)j * N16, D + 4 * j);
 }
 
 struct DecodeCtx {
@@ -77,6 +112,10 @@ struct DecodeCtx {
     float ref;                       // quantized scales: the column's range reference R
     float ref4[4];                   // the same for the four columns of a lane in the 16-row layout
     __amdgpu_buffer_rsrc_t rw, rs;   // weight and scale (or 4-bit scale code) buffers
+    // The same buffers with no valid byte: every load through them returns
+    // zeros without touching memory (the pipeline's steps past a run's end).
+    __amdgpu_buffer_rsrc_t rw0, rs0;
+    __amdgpu_buffer_rsrc_t rx;       // activations, M rows of K
 };
 
 // The group scale.  fp16 scales: the loaded value.  Quantized scales (QS):
@@ -107,27 +146,37 @@ template <int TC> struct Tile {
     static constexpr int CBSZ = TC == 64 ? 4 : 2;   // 16 or 4 blocks share one activation block
 };
 
-// Activation operand of row block rb.  TC = 64: lane (a = l/4, i = l%4) holds
-// x[4rb + i][128g + 8a .. +8).  TC = 16: lane (q, a = (l%16)/4, i) holds
-// x[4rb + i][128g + 32q + 8a .. +8).  Rows past M repeat row M-1 (unused).
+// Activation operand of row block rb: the per-lane byte offset in x of the
+// operand of group 0 (group g adds 256 g).  TC = 64: lane (a = l/4, i = l%4)
+// holds x[4rb + i][128g + 8a .. +8).  TC = 16: lane (q, a = (l%16)/4, i)
+// holds x[4rb + i][128g + 32q + 8a .. +8).  Rows past M repeat row M-1
+// (unused).
 template <int TC>
-__device__ __forceinline__ u4v load_act(const LinearDev& L, const DecodeCtx& c, int g, int rb) {
+__device__ __forceinline__ uint32_t act_offset(const LinearDev& L, const DecodeCtx& c, int rb) {
     const int a = (TC == 64 ? c.lane : (c.lane & 15)) >> 2, i = c.lane & 3;
     const int row = min(4 * rb + i, c.M - 1);
-    const size_t off = (size_t)row * L.K + (size_t)g * kGroup + (TC == 64 ? 0 : 32 * c.q) + 8 * a;
-    return *gptr<u4v>(L.x + off);
+    return 2u * ((uint32_t)row * (uint32_t)L.K + (TC == 64 ? 0u : 32u * (uint32_t)c.q) + 8u * (uint32_t)a);
 }
 
-// (c - z) * 2^(o-24) in both fp16 halves of a masked decoder-unit dword
-// holding c * 2^(o-24) (o = p0 * t, the unit's bit offset in its half):
-// one packed add of -z * 2^(o-24).  z << o < 2^10 for every width and
-// offset, so both operands and the sum are fp16 subnormals (or zero) on the
-// 2^-24 grid and the add is exact; c = z gives +0.
+// (c - z) * 2^-24 in both fp16 halves of a masked decoder-unit dword
+// holding c * 2^(o-24) (o = p0 * t, the unit's bit offset in its half): one
+// packed fp16 FMA, c * 2^(o-24) * 2^-o - z * 2^-24 (a packed add at o = 0).
+// c << o and z << o stay below 2^10 for every width and offset, so every
+// operand but the normal factor 2^-o, the exact product and the sum are
+// fp16 subnormals (or zero) on the 2^-24 grid: the single rounding is
+// exact, c = z gives +0, and units of every offset share one accumulator.
 template <int B, int O>
 __device__ __forceinline__ uint32_t unbias(uint32_t v) {
     static_assert(((1u << (B - 1)) << O) < 1024u, "zero point must stay subnormal");
-    constexpr uint32_t zb = 0x8000u | ((1u << (B - 1)) << O);
-    return __builtin_bit_cast(uint32_t, as_h2(v) + as_h2(zb | (zb << 16)));
+    constexpr uint32_t zb = 0x8000u | (1u << (B - 1));
+    const h2 bias = as_h2(zb | (zb << 16));
+    if constexpr (O == 0) {
+        return __builtin_bit_cast(uint32_t, as_h2(v) + bias);
+    } else {
+        constexpr _Float16 f = (_Float16)(1.0f / (float)(1u << O));
+        const h2 fv = {f, f};
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(as_h2(v), fv, bias));
+    }
 }
 
 template <int B, int MB, int TC, bool M1, bool QS>
@@ -135,34 +184,29 @@ __device__ __forceinline__ void group_compute(const DecodeCtx& c, const uint32_t
                                               const u4v (&X)[MB], uint16_t s16, float (&yacc)[MB][4]) {
     using TT = Tile<TC>;
     constexpr int C = Width<B>::per;
-    f4 acc[C][MB];
+    f4 acc[MB];
 #pragma unroll
-    for (int t = 0; t < C; ++t)
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) acc[t][rb] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < MB; ++rb) acc[rb] = f4{0.f, 0.f, 0.f, 0.f};
     static_for<0, TT::UNITS>([&](auto UC) {
         constexpr int U = decltype(UC)::value;
-        constexpr int t = U % C;
+        constexpr int O = Width<B>::p0 * (U % C);
         uint32_t b0, b1;
         unit_pair<B, U, TT::NQ>(Q, b0, b1);
-        const h4 bv = as_h4(unbias<B, Width<B>::p0 * t>(b0), unbias<B, Width<B>::p0 * t>(b1));
+        const h4 bv = as_h4(unbias<B, O>(b0), unbias<B, O>(b1));
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) {
             const h4 av = (U & 1) ? as_h4(X[rb][2], X[rb][3]) : as_h4(X[rb][0], X[rb][1]);
-            acc[t][rb] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, acc[t][rb], TT::CBSZ, U >> 1, 0);
+            acc[rb] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, acc[rb], TT::CBSZ, U >> 1, 0);
         }
     });
+    // The sums stay 2^-24 times too small until the wave's partials leave
+    // (kUnit): scaling by a power of two commutes exactly with every step.
     const float s = group_scale<B, QS>(c.ref, c.n, s16);
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
 #pragma unroll
         for (int r = 0; r < (M1 ? 1 : 4); ++r) {
-            if (M1 || 4 * rb + r < c.M) {
-                float tv = acc[0][rb][r] * class_factor<B>(0);
-#pragma unroll
-                for (int t = 1; t < C; ++t) tv = __builtin_fmaf(acc[t][rb][r], class_factor<B>(t), tv);
-                yacc[rb][r] = __builtin_fmaf(s, tv, yacc[rb][r]);
-            }
+            if (M1 || 4 * rb + r < c.M) yacc[rb][r] = __builtin_fmaf(s, acc[rb][r], yacc[rb][r]);
         }
     }
 }
@@ -187,52 +231,37 @@ template <int MB, int TC> struct Rows {
 // code 32j + 8kk + t of the group (units 2kk and 2kk + 1 of quarter j).  The
 // A operand is x in the same k order: lane (j, r) holds
 // x[r][128g + 32j + 8kk .. +8].  Lane (j, c) ends with rows 4j .. 4j + 3 of
-// its four columns.  Unit 2kk + 1 sits p0 bits above unit 2kk (the next
-// class); one shift puts both in unit 2kk's class, so each MFMA adds to one
-// class sum.  The zero point is removed from every weight (unbias) before
-// its MFMA.
+// its four columns.  Units 2kk and 2kk + 1 sit at different bit offsets;
+// unbias brings both to (c - z) * 2^-24 while removing the zero point, so
+// every MFMA of a column block adds to one sum.
 template <int B, bool QS>
 __device__ __forceinline__ void group_compute_mma(const DecodeCtx& c, const uint32_t (&Q)[4 * B], const u4v (&X)[4],
                                                   const uint16_t (&S)[4], float (&yacc)[4][4]) {
     using T = Width<B>;
-    constexpr int NCLS = T::per == 4 ? 2 : 1;   // classes 0 and 2 for 2- and 3-bit groups, else 0
-    f4 acc[4][NCLS];
+    f4 acc[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int k = 0; k < NCLS; ++k) acc[cb][k] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < 4; ++cb) acc[cb] = f4{0.f, 0.f, 0.f, 0.f};
     static_for<0, 4>([&](auto KC) {
         constexpr int kk = decltype(KC)::value;
-        constexpr int cls = NCLS == 2 ? (kk & 1) : 0;
-        constexpr int O = T::p0 * ((2 * kk) % T::per);   // bit offset of unit 2kk (and, shifted, 2kk + 1)
+        constexpr int O0 = T::p0 * ((2 * kk) % T::per);       // bit offsets of units 2kk and 2kk + 1
+        constexpr int O1 = T::p0 * ((2 * kk + 1) % T::per);
         const h8 xop = __builtin_bit_cast(h8, X[kk]);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             uint32_t a0, a1, b0, b1;
             unit_pair<B, 2 * kk, 1>(Q + cb * B, a0, a1);
             unit_pair<B, 2 * kk + 1, 1>(Q + cb * B, b0, b1);
-            if constexpr (T::per >= 2) {
-                b0 >>= T::p0;
-                b1 >>= T::p0;
-            }
             const h8 wop = __builtin_bit_cast(
-                h8, u4v{unbias<B, O>(a0), unbias<B, O>(a1), unbias<B, O>(b0), unbias<B, O>(b1)});
-            acc[cb][cls] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, wop, acc[cb][cls], 0, 0, 0);
+                h8, u4v{unbias<B, O0>(a0), unbias<B, O0>(a1), unbias<B, O1>(b0), unbias<B, O1>(b1)});
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, wop, acc[cb], 0, 0, 0);
         }
     });
-    // Each class's factor goes into the scale (exact: a power of two times an
-    // fp16 value), so each row takes one product per class.
+    // Sums 2^-24 times too small, as in group_compute.
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const float s = group_scale<B, QS>(c.ref4[cb], c.n + 16 * cb, S[cb]);
-        const float s0 = s * class_factor<B>(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) yacc[cb][i] = __builtin_fmaf(s0, acc[cb][0][i], yacc[cb][i]);
-        if constexpr (NCLS == 2) {
-            const float s2 = s * class_factor<B>(2);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) yacc[cb][i] = __builtin_fmaf(s2, acc[cb][1][i], yacc[cb][i]);
-        }
+        for (int i = 0; i < 4; ++i) yacc[cb][i] = __builtin_fmaf(s, acc[cb][i], yacc[cb][i]);
     }
 }
 
@@ -299,7 +328,8 @@ __device__ __forceinline__ void run_width_mma_ring(const LinearDev& L, const Dec
     // the copies count as memory writes.
     const __attribute__((address_space(4))) uint32_t* og = (const __attribute__((address_space(4))) uint32_t*)ord;
     const uint32_t N16 = 16u * (uint32_t)L.N;
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(L.x, 2u * (uint32_t)c.M * (uint32_t)L.K);
+    const QuarterOffsets qo = quarter_offsets<B>(16u * (uint32_t)c.n, c.q, N16);
+    const uint32_t sv = QS ? (uint32_t)c.n >> 1 : 2u * (uint32_t)c.n;   // the lane's scale, column block 0
     uint32_t xv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -310,23 +340,19 @@ __device__ __forceinline__ void run_width_mma_ring(const LinearDev& L, const Dec
         const bool valid = step < cnt;
         const uint32_t e = og[min(step, cnt - 1)];
         const uint32_t g = e & 0xFFFFu, P = e >> 16;
+        const __amdgpu_buffer_rsrc_t rw = valid ? c.rw : c.rw0, rs = valid ? c.rs : c.rs0;
         char* dst = ring + slot * kXSlot;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(dst + 1024 * i), 16, (int)xv[i], (int)(256u * g),
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (lds_ptr_t)(dst + 1024 * i), 16, (int)xv[i],
+                                                     (int)(256u * g), 0, 0);
+        // Column block cb: columns n + 16 cb, 256 cb bytes on in every word
+        // row, 16 cb scales on.
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            const uint32_t n = (uint32_t)(c.n + 16 * cb);
-            const uint32_t col = valid ? 16u * ((uint32_t)L.N * P + n) : kBufOOB;
-            load_quarter<B>(c.rw, col, N16, c.q, *reinterpret_cast<uint32_t(*)[B]>(Qd + cb * B));
-            if constexpr (QS) {
-                const uint32_t soff = valid ? g * ((uint32_t)L.N >> 1) + (n >> 1) : kBufOOB;
-                Sd[cb] = __builtin_amdgcn_raw_buffer_load_b8(c.rs, soff, 0, 0);
-            } else {
-                const uint32_t soff = valid ? 2u * (g * (uint32_t)L.N + n) : kBufOOB;
-                Sd[cb] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, soff, 0, 0);
-            }
+            load_quarter<B>(rw, qo, N16 * P + 256u * cb, N16, *reinterpret_cast<uint32_t(*)[B]>(Qd + cb * B));
+            if constexpr (QS) Sd[cb] = __builtin_amdgcn_raw_buffer_load_b8(rs, sv, g * ((uint32_t)L.N >> 1) + 8u * cb, 0);
+            else Sd[cb] = __builtin_amdgcn_raw_buffer_load_b16(rs, sv, 2u * g * (uint32_t)L.N + 32u * cb, 0);
         }
     };
     // Group in slot k once at most `wait` loads are in flight.
@@ -359,8 +385,10 @@ __device__ __forceinline__ void run_width_mma_ring(const LinearDev& L, const Dec
 // while group i is computed, groups i+1 .. i+DEPTH-1 are in flight.  Every
 // step issues exactly one group's loads -- weights, scale, activation
 // operands, in that order -- so each wait is a compile-time count.  Steps
-// past the end of the run load from an out-of-range buffer offset: they
-// keep the count fixed, return zeros and cost no memory traffic.
+// past the end of the run load through buffer descriptors of size zero:
+// they keep the count fixed, return zeros and cost no memory traffic.  Only
+// the uniform parts of the offsets change from group to group (scalar
+// offsets); the per-lane parts are set once per run.
 template <int B, int MB, int TC, bool M1, bool QS, bool XR, bool WIDE = false>
 __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c, const uint32_t* ord, int cnt,
                                           float (&yacc)[Rows<MB, TC>::YB][4], char* ring) {
@@ -381,33 +409,38 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
     u4v X[DEPTH][NX];
     const EXQ_GLOBAL uint32_t* og = gptr<uint32_t>(ord);
     const uint32_t N16 = 16u * (uint32_t)L.N;
+    // Per-lane parts of every load's offset (the uniform parts come with the
+    // group): weights, scale, activations.
+    const QuarterOffsets qo = quarter_offsets<B>(16u * (uint32_t)c.n, c.q, N16);
+    const uint32_t sv = QS ? (uint32_t)c.n >> 1 : 2u * (uint32_t)c.n;
+    uint32_t xv[MMA ? 1 : MB];
+    if constexpr (MMA) {
+        // Lane (j, r) reads x[r][128g + 32j ..]; rows past M repeat row M-1 (unused).
+        xv[0] = 2u * ((uint32_t)min(c.lane & 15, c.M - 1) * (uint32_t)L.K + 32u * (uint32_t)c.q);
+    } else {
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) xv[rb] = act_offset<TC>(L, c, rb);
+    }
     auto issue = [&](int step, uint32_t (&Qd)[NDW], uint16_t (&Sd)[NS], u4v (&Xd)[NX]) {
         const bool valid = step < cnt;
         const uint32_t e = og[min(step, cnt - 1)];
         const uint32_t g = e & 0xFFFFu, P = e >> 16;
+        const __amdgpu_buffer_rsrc_t rw = valid ? c.rw : c.rw0, rs = valid ? c.rs : c.rs0;
 #pragma unroll
         for (int cb = 0; cb < NS; ++cb) {
-            const uint32_t n = (uint32_t)(c.n + 16 * cb);
-            const uint32_t col = valid ? 16u * ((uint32_t)L.N * P + n) : kBufOOB;
-            if constexpr (MMA) load_quarter<B>(c.rw, col, N16, c.q, *reinterpret_cast<uint32_t(*)[B]>(Qd + cb * B));
-            else if constexpr (TC == 64) load_group_words<B>(c.rw, col, N16, Qd);
-            else load_quarter<B>(c.rw, col, N16, c.q, Qd);
-            if constexpr (QS) {
-                const uint32_t soff = valid ? g * ((uint32_t)L.N >> 1) + (n >> 1) : kBufOOB;
-                Sd[cb] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b8(c.rs, soff, 0, 0);
-            } else {
-                const uint32_t soff = valid ? 2u * (g * (uint32_t)L.N + n) : kBufOOB;
-                Sd[cb] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(c.rs, soff, 0, 0);
-            }
+            const uint32_t wo = N16 * P + 256u * cb;   // column block cb: columns n + 16 cb
+            if constexpr (MMA) load_quarter<B>(rw, qo, wo, N16, *reinterpret_cast<uint32_t(*)[B]>(Qd + cb * B));
+            else if constexpr (TC == 64) load_group_words<B>(rw, 16u * (uint32_t)c.n, wo, N16, Qd);
+            else load_quarter<B>(rw, qo, wo, N16, Qd);
+            if constexpr (QS) Sd[cb] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b8(rs, sv, g * ((uint32_t)L.N >> 1) + 8u * cb, 0);
+            else Sd[cb] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, sv, 2u * g * (uint32_t)L.N + 32u * cb, 0);
         }
         if constexpr (MMA) {
-            const int row = min(c.lane & 15, c.M - 1);   // rows past M repeat row M-1 (unused)
-            const EXQ_GLOBAL u4v* xr = gptr<u4v>(L.x + (size_t)row * L.K + (size_t)g * kGroup + 32 * c.q);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) Xd[kk] = xr[kk];
+            for (int kk = 0; kk < 4; ++kk) Xd[kk] = __builtin_amdgcn_raw_buffer_load_b128(c.rx, xv[0], 256u * g + 16u * kk, 0);
         } else {
 #pragma unroll
-            for (int rb = 0; rb < MB; ++rb) Xd[rb] = load_act<TC>(L, c, (int)g, rb);
+            for (int rb = 0; rb < MB; ++rb) Xd[rb] = __builtin_amdgcn_raw_buffer_load_b128(c.rx, xv[rb], 256u * g, 0);
         }
     };
     static_for<0, DEPTH - 1>([&](auto KC) {
@@ -479,11 +512,14 @@ __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int 
     c.q = (TC == 64 && !MMA) ? 0 : lane >> 4;
     c.n = tile * TC + ((TC == 64 && !MMA) ? lane : (lane & 15));
     c.rw = buffer_rsrc(L.qweight, L.qbytes);
+    c.rw0 = buffer_rsrc(L.qweight, 0);
+    c.rx = buffer_rsrc(L.x, 2u * (uint32_t)M * (uint32_t)L.K);
     c.ref = 0.0f;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) c.ref4[cb] = 0.0f;
     if constexpr (QS) {
         c.rs = buffer_rsrc(L.qscale, L.qsbytes);
+        c.rs0 = buffer_rsrc(L.qscale, 0);
         if constexpr (MMA) {
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
@@ -493,6 +529,7 @@ __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int 
         }
     } else {
         c.rs = buffer_rsrc(L.scales, L.sbytes);
+        c.rs0 = buffer_rsrc(L.scales, 0);
     }
 
     float yacc[YB][4];
@@ -525,7 +562,7 @@ __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * c.q + i;
-                if (row < M) red[(wave * M + row) * TC + (lane & 15) + 16 * cb] = yacc[cb][i];
+                if (row < M) red[(wave * M + row) * TC + (lane & 15) + 16 * cb] = yacc[cb][i] * kUnit;
             }
         return;
     }
@@ -535,7 +572,7 @@ __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int 
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float v = yacc[rb][r];
+            float v = yacc[rb][r] * kUnit;
             if constexpr (TC == 16) {
                 v += __shfl_xor(v, 16);
                 v += __shfl_xor(v, 32);
@@ -653,8 +690,9 @@ template <int B>
 __device__ __forceinline__ void dequant_quarter(const LinearDev& L, size_t P, int g, int n, int q,
                                                 uint16_t* __restrict__ w_out) {
     uint32_t Q[B];
-    load_quarter<B>(buffer_rsrc(L.qweight, L.qbytes), 16u * ((uint32_t)L.N * (uint32_t)P + (uint32_t)n),
-                    16u * (uint32_t)L.N, q, Q);
+    const uint32_t N16 = 16u * (uint32_t)L.N;
+    load_quarter<B>(buffer_rsrc(L.qweight, L.qbytes), quarter_offsets<B>(16u * (uint32_t)n, q, N16),
+                    N16 * (uint32_t)P, N16, Q);
     const uint16_t s16 = *gptr<uint16_t>(L.scales + (size_t)g * L.N + n);
     const float s = (float)__builtin_bit_cast(_Float16, s16);
     constexpr int C = Width<B>::per;

@@ -114,29 +114,6 @@ __device__ __forceinline__ void unit_pair(const uint32_t* Q, uint32_t& b0, uint3
     }
 }
 
-// Loads the B dwords of quarter q of the column whose word 0 (of this group)
-// is at byte `col` of the weight buffer (kBufOOB: a tail step, zeros).  Plane
-// p occupies column-local dwords [m0 + q*p, m0 + (q+1)*p): a p-dword piece of
-// one 16-byte word for p <= 4, two whole words for p = 8.  nt: streamed once.
-template <int P_DW>
-__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t rw, uint32_t col, uint32_t N16, int m,
-                                           uint32_t* dst) {
-    const uint32_t off = col + (uint32_t)(m >> 2) * N16 + 4u * (uint32_t)(m & 3);
-    if constexpr (P_DW == 1) {
-        dst[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, off, 0, 2);
-    } else if constexpr (P_DW == 2) {
-        const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, 2);
-        dst[0] = v[0];
-        dst[1] = v[1];
-    } else {
-        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 2);
-        dst[0] = v[0];
-        dst[1] = v[1];
-        dst[2] = v[2];
-        dst[3] = v[3];
-    }
-}
-
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // fp16 pair view of a dword.  The argument is a plain scalar on purpose:

@@ -281,6 +281,16 @@ __device__ __forceinline__ void tail_steps(int rem, F&& f) {
     }
 }
 
+// Empty volatile asm statements that take every element of r as input and
+// output: work that reads r cannot start before them, work that writes r
+// cannot end after them, and, having side effects, they keep their place
+// among the loads of the pipeline.
+template <class T, int N>
+__device__ __forceinline__ void pin_regs(T (&r)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+}
+
 template <int B, int TC, bool WIDE = false> struct Depth {
     // groups in flight per wave (the one being computed included); WIDE:
     // the high-occupancy plan kernel (8 waves per SIMD, 64 VGPRs)
@@ -407,7 +417,9 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
     uint32_t Q[DEPTH][NDW];
     uint16_t S[DEPTH][NS];
     u4v X[DEPTH][NX];
-    const EXQ_GLOBAL uint32_t* og = gptr<uint32_t>(ord);
+    // Read-only for the kernel: a constant-space load stays scalar whatever
+    // the compiler can prove about the memory the kernel writes.
+    const __attribute__((address_space(4))) uint32_t* og = (const __attribute__((address_space(4))) uint32_t*)ord;
     const uint32_t N16 = 16u * (uint32_t)L.N;
     // Per-lane parts of every load's offset (the uniform parts come with the
     // group): weights, scale, activations.
@@ -449,8 +461,16 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
     });
     auto compute = [&](auto KC) {
         constexpr int k = decltype(KC)::value;
+        if constexpr (!MMA) {
+            pin_regs(Q[k]);
+            pin_regs(X[k]);
+        }
         if constexpr (MMA) group_compute_mma<B, QS>(c, Q[k], X[k], S[k], yacc);
         else group_compute<B, MB, TC, M1, QS>(c, Q[k], X[k], S[k][0], yacc);
+        if constexpr (!MMA) {
+#pragma unroll
+            for (int rb = 0; rb < Rows<MB, TC>::YB; ++rb) pin_regs(yacc[rb]);
+        }
     };
     if constexpr (MMA && B >= 5) {
         // The 16-row layout's wide groups (4b code dwords per group in
@@ -474,9 +494,12 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
         return;
     }
     // Whole rounds of DEPTH steps with no exit inside, then the last partial
-    // round (see tail_steps).  Scheduling barriers close each step (and, for
-    // M <= 4, keep its loads ahead of its compute), so a step's loads stay
-    // in their step.
+    // round (see tail_steps).  Scheduling barriers close each step; for
+    // M <= 4 the compute is also pinned between its inputs and its partial
+    // sums (pin_regs).  Scheduling barriers alone do not hold arithmetic: the
+    // compiler gathered a round's computes between its first and its other
+    // issues, so the last group of every round waited for a load issued just
+    // before it.
     int i = 0;
     for (; i + DEPTH <= cnt; i += DEPTH) {
         static_for<0, DEPTH>([&](auto KC) {

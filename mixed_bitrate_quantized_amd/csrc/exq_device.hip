@@ -417,9 +417,12 @@ __device__ __forceinline__ void run_width(const LinearDev& L, const DecodeCtx& c
     uint32_t Q[DEPTH][NDW];
     uint16_t S[DEPTH][NS];
     u4v X[DEPTH][NX];
-    // Read-only for the kernel: a constant-space load stays scalar whatever
-    // the compiler can prove about the memory the kernel writes.
-    const __attribute__((address_space(4))) uint32_t* og = (const __attribute__((address_space(4))) uint32_t*)ord;
+    // Read-only for the kernel.  For M <= 4 a constant-space load keeps the
+    // entries scalar beside the pinning asm statements (which count as memory
+    // side effects); the 16-row layout keeps the global view, with which its
+    // wide groups fit their registers.
+    using OrdPtr = std::conditional_t<MMA, const EXQ_GLOBAL uint32_t*, const __attribute__((address_space(4))) uint32_t*>;
+    const OrdPtr og = (OrdPtr)ord;
     const uint32_t N16 = 16u * (uint32_t)L.N;
     // Per-lane parts of every load's offset (the uniform parts come with the
     // group): weights, scale, activations.

@@ -241,10 +241,13 @@ def allocator_leg(exq, kept, nblk):
                         "the seeded schedule's budget (2.55 bpw per linear), its >= 6-bit groups kept" % nblk}
 
 
-def qs_leg(exq, torch, M, steps, stream, nblk=8):
+def qs_leg(exq, torch, M, steps, stream, fp16_plans, nblk=8, rounds=3):
     """Decode with quantized group scales (4-bit codes + a column reference):
     `nblk` 70B-shaped blocks (2.2 GB, well above the Infinity Cache) packed with
-    exq_pack_qs, one plan launch per block, rotating over the blocks."""
+    exq_pack_qs, one plan launch per block, rotating over the blocks.  The same
+    number of fp16-scale block plans of the same shapes (`fp16_plans`) is timed
+    in alternation with them, `rounds` times each, so that both figures come
+    from the same stretch of the run (clock and cache state alike)."""
     from synth import BLOCK_SHAPES, workloads
     specs = workloads.linears(5)[: nblk * len(BLOCK_SHAPES)]
     layers, xs, ys, nbytes = [], [], [], 0
@@ -258,31 +261,39 @@ def qs_leg(exq, torch, M, steps, stream, nblk=8):
         G = spec.K // 128
         nbytes += q.size + qsc.size + 2 * spec.N + 5 * G + 2 * M * spec.K + 2 * M * spec.N
     plans = [exq.Plan(layers[b * 7:(b + 1) * 7], xs[b * 7:(b + 1) * 7], ys[b * 7:(b + 1) * 7], M) for b in range(nblk)]
-
-    def step():
-        for p in plans:
-            p.run(stream)
-
-    for _ in range(10):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = max(steps, 40)
-    e0.record(stream)
-    for _ in range(reps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us_block = e0.elapsed_time(e1) * 1e3 / (reps * nblk)
+
+    def timed(ps):
+        for _ in range(10):
+            for p in ps:
+                p.run(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for p in ps:
+                p.run(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * len(ps))
+
+    qs_us, fp_us = [], []
+    for _ in range(rounds):
+        qs_us.append(timed(plans))
+        fp_us.append(timed(fp16_plans[:nblk]))
+    us_block, fp_block = float(np.median(qs_us)), float(np.median(fp_us))
     for p in plans:
         p.close()
     for l in layers:
         l.close()
     per_block = nbytes / nblk
-    log("quantized scales: %.1f us per block, %.0f B per block" % (us_block, per_block))
+    log("quantized scales: %.1f us per block (fp16 scales, same shapes, alternated: %.1f us), %.0f B per block" % (
+        us_block, fp_block, per_block))
     return {"workload": "%d llama3-70b-shaped blocks, 2.55 bpw, 4-bit group scale codes, M=%d, one plan per block" % (nblk, M),
             "us_per_block": round(us_block, 2), "bytes_per_block": int(per_block),
             "GB/s": round(per_block / (us_block * 1e-6) / 1e9, 1),
+            "fp16_scales_us_per_block_same_blocks": round(fp_block, 2),
+            "timing": "median over %d alternated rounds of %d steps over the %d blocks, each after 10 warmup steps" % (
+                rounds, reps, nblk),
             "ms_per_step_80_blocks_equivalent": round(us_block * 80 / 1e3, 4)}
 
 
@@ -808,8 +819,8 @@ def main():
 
     qsres = None
     if not args.no_qs and args.config == 5:
-        qsres = qs_leg(exq, torch, M, args.steps, stream)
-        qsres["fp16_scales_us_per_block"] = round(ms_step * 1e3 / nblk, 2)
+        qsres = qs_leg(exq, torch, M, args.steps, stream, plans, nblk=min(8, len(plans)))
+        qsres["fp16_scales_us_per_block_whole_stack"] = round(ms_step * 1e3 / nblk, 2)
 
     tune = None
     if not args.no_autotune:

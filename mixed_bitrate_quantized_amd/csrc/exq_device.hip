@@ -109,7 +109,7 @@ __device__ __forceinline__ void load_group_words(__amdgpu_buffer_rsrc_t rw, uint
 
 struct DecodeCtx {
     int M, lane, q, n;
-    float ref;                       // quantized scales: the column's range reference R
+    float ref;                       // quantized scales: the column's range reference R / 256 (exact)
     float ref4[4];                   // the same for the four columns of a lane in the 16-row layout
     __amdgpu_buffer_rsrc_t rw, rs;   // weight and scale (or 4-bit scale code) buffers
     // The same buffers with no valid byte: every load through them returns
@@ -121,7 +121,8 @@ struct DecodeCtx {
 // The group scale.  fp16 scales: the loaded value.  Quantized scales (QS):
 // the loaded byte holds the column's 4-bit code q in its low (even column)
 // or high (odd column) nibble, and s = fp16_RNE(fp32(t * fp32(1/(2^(b-1)-1))))
-// with t = R (q+1)^2 / 256, exact in fp32.
+// with t = R (q+1)^2 / 256, exact in fp32; ref holds R / 256, so t is one
+// exact product.
 template <int B, bool QS>
 __device__ __forceinline__ float group_scale(float ref, int n, uint16_t raw) {
     if constexpr (!QS) {
@@ -133,7 +134,7 @@ __device__ __forceinline__ float group_scale(float ref, int n, uint16_t raw) {
         // mixed-precision multiply (v_fma_mixlo_f16) that rounds once, to fp16.
         constexpr float inv = 1.0f / (float)((1 << (B - 1)) - 1);
         const int q1 = (int)((raw >> (4 * (n & 1))) & 15u) + 1;
-        const float t = ref * (float)(q1 * q1) * 0.00390625f;
+        const float t = ref * (float)(q1 * q1);
         float u = t * inv;
         asm("" : "+v"(u));
         return (float)(_Float16)u;
@@ -303,7 +304,9 @@ template <int B, int TC, bool WIDE = false> struct Depth {
 // pipelines instead of two with deeper ones.  On the 70B block (1312
 // workgroups) it measured 5 % faster at M = 1 and M = 4; a single linear
 // (fewer workgroups than CUs) took twice as long with it, its waves' own
-// pipelines being all that hides the memory latency.
+// pipelines being all that hides the memory latency.  Plans of layers with
+// quantized scales run it too: with the pipeline steps pinned it took 8
+// such blocks from 59.7-60.0 to 56.7-57.5 us per block.
 constexpr int kWideWgsPerCu = 4;
 
 // Activation ring of the 16-row layout in decode and plan launches: two
@@ -549,9 +552,9 @@ __device__ __forceinline__ void decode_stream(const LinearDev& L, int tile, int 
         if constexpr (MMA) {
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
-                c.ref4[cb] = (float)__builtin_bit_cast(_Float16, gptr<uint16_t>(L.ref)[c.n + 16 * cb]);
+                c.ref4[cb] = (float)__builtin_bit_cast(_Float16, gptr<uint16_t>(L.ref)[c.n + 16 * cb]) * 0.00390625f;
         } else {
-            c.ref = (float)__builtin_bit_cast(_Float16, gptr<uint16_t>(L.ref)[c.n]);
+            c.ref = (float)__builtin_bit_cast(_Float16, gptr<uint16_t>(L.ref)[c.n]) * 0.00390625f;
         }
     } else {
         c.rs = buffer_rsrc(L.scales, L.sbytes);
@@ -1462,8 +1465,7 @@ exq_status exq_plan_create(int count, const exq_layer_t* layers, const void* con
             exq_plan_destroy(P);
             return hip_fail(e, "compute unit count");
         }
-        // fp16 scales only: with quantized scales it measured slower than the deep kernel.
-        P->wide = !P->qs && P->total_wgs >= kWideWgsPerCu * cus;
+        P->wide = P->total_wgs >= kWideWgsPerCu * cus;
     }
     if ((e = hipMalloc(&P->d_list, sizeof(LinearDev) * count)) != hipSuccess ||
         (e = hipMalloc(&P->d_wg_map, sizeof(uint32_t) * wg_map.size())) != hipSuccess) {

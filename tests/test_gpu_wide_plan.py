@@ -6,7 +6,8 @@ workgroups per CU with shallower pipelines.  These plans hold enough tiles
 for it on any device of up to 256 CUs (1024 or more tiles) while keeping K
 small for the oracle: every output is checked, at M = 1, 2 and 4, with and
 without the zero-point edge structure (zero-code weights under large
-activations), and a second run must repeat the first bit for bit.
+activations), with fp16 and with quantized group scales, and a second run
+must repeat the first bit for bit.
 """
 import numpy as np
 import pytest
@@ -48,9 +49,10 @@ def edge_case(rng, M, N, K):
 
 @pytest.mark.parametrize("M", [1, 2, 4])
 @pytest.mark.parametrize("edge", [False, True], ids=["normal", "zero-point-edge"])
-def test_large_decode_plan(exq, M, edge):
+@pytest.mark.parametrize("qs", [False, True], ids=["fp16-scales", "quantized-scales"])
+def test_large_decode_plan(exq, M, edge, qs):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    rng = np.random.default_rng(7 * M + edge)
+    rng = np.random.default_rng(7 * M + edge + 100 * qs)
     N = 8192
     count = max(8, -(-4 * cus // (N // 64)))   # at least 4 tiles per CU
     layers, refs, xs_h = [], [], []
@@ -62,22 +64,29 @@ def test_large_decode_plan(exq, M, edge):
             W, x_edge = edge_case(rng, M, N, K)
         else:
             W = synth.weight(synth.seed_for("wide-plan", M, i), N, K)
-        q, s = exq.exq_pack(W, widths)
-        codes, s_ref, q_ref = oracle.reference_layer(W, widths)
-        np.testing.assert_array_equal(q, q_ref)
-        layers.append(exq.Layer(K, N, widths, q, s))
+        if qs:
+            q, qsc, ref = exq.exq_pack_qs(W, widths)
+            codes, R, qs_o, s_ref = oracle.quantize_qs(W, widths)
+            np.testing.assert_array_equal(qsc, qs_o)
+            np.testing.assert_array_equal(ref, R)
+            layers.append(exq.Layer(K, N, widths, q, qsc, ref=ref))
+        else:
+            q, s = exq.exq_pack(W, widths)
+            codes, s_ref, q_ref = oracle.reference_layer(W, widths)
+            np.testing.assert_array_equal(q, q_ref)
+            layers.append(exq.Layer(K, N, widths, q, s))
         refs.append(oracle.dequant(codes, s_ref, widths))
         xs_h.append(x_edge if edge else synth.activations(synth.seed_for("wide-plan-x", M, i), M, K))
     xs = [to_dev(x) for x in xs_h]
     ys = [torch.empty((M, N), dtype=torch.float16, device="cuda") for _ in layers]
-    note("wide plan: %d linears x %d tiles, M=%d edge=%d (%d CUs)" % (count, N // 64, M, edge, cus))
+    note("wide plan: %d linears x %d tiles, M=%d edge=%d qs=%d (%d CUs)" % (count, N // 64, M, edge, qs, cus))
     plan = exq.Plan(layers, xs, ys, M)
     try:
         plan.run()
         got = [y_to_np(y).copy() for y in ys]
         for i, (x, w_ref, g) in enumerate(zip(xs_h, refs, got)):
             y_ref, bnd = oracle.gemm(x, w_ref)
-            assert_within(g, y_ref, bnd, "wide plan linear %d M=%d edge=%d" % (i, M, edge))
+            assert_within(g, y_ref, bnd, "wide plan linear %d M=%d edge=%d qs=%d" % (i, M, edge, qs))
         plan.run()
         for y, g in zip(ys, got):
             np.testing.assert_array_equal(y_to_np(y), g)

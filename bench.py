@@ -14,7 +14,8 @@ bounded sample of the same workload.  Further legs:
     block's data flow allows (q/k/v plan, o, fused gate/up, down);
   * prefill: the same seven 70B shapes at M = 2048 tokens (mixed 4.0 bpw
     from {3,4,5,6}) against the fp16 matrix-core peak, with the oracle timed
-    on 64 seeded token rows;
+    on 64 seeded token rows and, as context, plain fp16 library GEMMs
+    (torch.matmul) on the dequantized weights of the same shapes;
   * batched_decode_m16: the same stack at M = 16 rows;
   * single_layer: configurations 1 (4096 x 4096, 4-bit, M = 1) and 2
     (8192 x 8192, 2.55 bpw, M = 1/4/8/16), rotating over >= 1 GiB of copies;
@@ -427,7 +428,7 @@ def prefill_oracle_subset(kept, xs, ys, rows_n, seed):
     return secs, flops, worst
 
 
-def prefill_leg(exq, torch, steps, warmup, oracle_rows=64):
+def prefill_leg(exq, torch, steps, warmup, oracle_rows=64, dense_ref=True):
     """The seven 70B-shaped linears at M = 2048 (mixed 4.0 bpw) as one prefill
     plan launch per step; step time, the launch's own duration, and the same
     step as seven separate exq_gemm calls for reference.  The oracle is timed
@@ -459,6 +460,26 @@ def prefill_leg(exq, torch, steps, warmup, oracle_rows=64):
         for l, x, y in zip(layers, xs, ys):
             exq.exq_gemm(x.data_ptr(), M, l.handle, y.data_ptr(), stream)
     ms_calls = timed(calls, max(3, steps // 2))
+
+    # Context, not the path: the same seven products as plain fp16 library
+    # GEMMs (torch.matmul, which calls hipBLASLt / rocBLAS) on the dequantized
+    # weights W_hat [K][N], a practical matrix-core ceiling for these shapes.
+    dense = None
+    if dense_ref:
+        ws = [l.dequant(stream) for l in layers]
+        dys = [torch.empty_like(y) for y in ys]
+
+        def dense_step():
+            for x, w, y in zip(xs, ws, dys):
+                torch.matmul(x, w, out=y)
+        ms_dense = timed(dense_step, max(3, steps // 2))
+        dense = {"ms_per_step": round(ms_dense, 4), "TFLOP/s": round(flops / (ms_dense * 1e-3) / 1e12, 2),
+                 "pct_of_peak": round(100 * flops / (ms_dense * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 2),
+                 "kernel": "torch.matmul (hipBLASLt / rocBLAS) fp16 x fp16 -> fp16, 7 calls on the dequantized weights",
+                 "weight_bytes_fp16": int(sum(w.numel() * 2 for w in ws))}
+        del ws, dys
+        torch.cuda.empty_cache()
+        log("dense fp16 library GEMMs on W_hat: %.3f ms per step, %.1f TFLOP/s" % (ms_dense, dense["TFLOP/s"]))
     cpu = None
     if oracle_rows:
         plan.run(stream)
@@ -490,6 +511,7 @@ def prefill_leg(exq, torch, steps, warmup, oracle_rows=64):
         "unit": "TFLOP/s",
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_separate_calls": round(ms_calls, 4),
+        "dense_fp16_library_gemm": dense,
         "steps": steps,
         "warmup": warmup,
         "flops_per_step": flops,
@@ -649,6 +671,7 @@ def main():
     ap.add_argument("--no-allocator", action="store_true", help="skip the host bit-allocation leg")
     ap.add_argument("--no-autotune", action="store_true", help="skip the per-shape kernel-choice leg")
     ap.add_argument("--no-qs", action="store_true", help="skip the quantized-scale decode leg")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense fp16 library GEMM context of the prefill leg")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="run a plain device copy of this size (for counter calibration) and exit")
     args = ap.parse_args()
@@ -838,7 +861,8 @@ def main():
             l.close()
         del layers, xs, ys, plans
         torch.cuda.empty_cache()
-        prefill = prefill_leg(exq, torch, args.prefill_steps, args.prefill_warmup, args.prefill_oracle_rows)
+        prefill = prefill_leg(exq, torch, args.prefill_steps, args.prefill_warmup, args.prefill_oracle_rows,
+                              dense_ref=not args.no_dense)
 
     single = None
     if not args.no_single:

@@ -170,8 +170,10 @@ exq_status exq_allocate_widths(const double* err, const int32_t* size, int G, in
  * The handle owns a few kilobytes of device metadata (the per-group offsets
  * and the width-sorted visiting order); it holds no scratch state, so any
  * number of streams may use it at once.  Errors: INVALID_ARG, UNSUPPORTED
- * (group_size != 128, or K so large that one workgroup's activation sums do
- * not fit in LDS), OOM, HIP. */
+ * (group_size != 128; 65536 or more 16-byte words per column, i.e.
+ * sum(widths) >= 65536, which the 16-bit per-column word offsets cannot
+ * address; 2 GiB or more of packed words, beyond the 32-bit buffer offsets),
+ * OOM, HIP.  Every argument is checked before anything is allocated. */
 exq_status exq_layer_create(int K, int N, int group_size, const uint8_t* widths_host,
                             const void* d_qweight, const void* d_scales, exq_layer_t* out);
 

@@ -187,3 +187,13 @@ def test_layer_create_accepts_n_multiple_of_16():
         assert st in (exq.EXQ_OK, exq.EXQ_ERR_OOM, exq.EXQ_ERR_HIP), (N, st)
         if st == exq.EXQ_OK:
             exq.exq_layer_destroy(h.value)
+
+
+def test_layer_size_limits_are_unsupported():
+    """Valid shapes beyond the layer limits fail with EXQ_ERR_UNSUPPORTED
+    before anything is allocated: 65536 or more 16-byte words per column
+    (16-bit word offsets), and 2 GiB or more of packed words (32-bit buffer
+    offsets)."""
+    fake = 0x10000  # never dereferenced
+    _expect(exq.EXQ_ERR_UNSUPPORTED, exq.exq_layer_create, 128 * 8192, 16, np.full(8192, 8, np.uint8), fake, fake)
+    _expect(exq.EXQ_ERR_UNSUPPORTED, exq.exq_layer_create, 128 * 2048, 32768, np.full(2048, 2, np.uint8), fake, fake)
